@@ -1,0 +1,136 @@
+// C ABI of the attention library: argument validation, workspace layout and dispatch to the
+// kernel launchers. Every check runs before the first HIP call, so an invalid call launches
+// nothing and touches no device state.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_kernels.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool valid_dtype(int t) { return t == FA_F32 || t == FA_F16 || t == FA_BF16; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shared shape checks. Returns FA_OK or the status to report.
+fa_status check_shape(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
+  const long long elems = (long long)B * H * N * d;
+  if (elems > 0x7FFFFFFFLL) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+// scale * log2(e) as used by the kernels. scale == 0 (uniform attention) maps to a tiny
+// positive factor: every exponent then rounds to exactly 2^0 in fp32, which is the same result.
+float log2_scale(float scale) {
+  const float c = scale * kLog2e;
+  return c == 0.f ? 1e-30f : c;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t workspace_layout(int B, int H, int N, int d, fa_dtype grad_dtype, size_t* dq_off) {
+  const size_t rows = (size_t)B * H * N;
+  const size_t delta_bytes = round_up(rows * sizeof(float), 256);
+  *dq_off = delta_bytes;
+  const size_t dq_bytes = (grad_dtype == FA_F32) ? 0 : rows * (size_t)d * sizeof(float);
+  return delta_bytes + dq_bytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument (null or misaligned pointer, bad size, non-finite scale, bad flag)";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim, dtype combination or mode not provided by this library";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case FA_ERR_HIP: return "FA_ERR_HIP: a HIP runtime call or kernel launch failed";
+  }
+  return "unknown fa_status";
+}
+
+fa_status fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int H, int N, int d, float scale, int causal, fa_dtype in_dtype,
+                     fa_dtype o_dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_INVALID_ARG;
+  if (!valid_dtype(in_dtype) || !valid_dtype(o_dtype)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+  const fa_status st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (o_dtype != in_dtype && o_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+
+  fa::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.N = N;
+  a.bh = B * H;
+  a.c = log2_scale(scale);
+  const hipError_t e = fa::launch_forward(a, d, (int)in_dtype, o_dtype == FA_F32 ? 1 : 0,
+                                          causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_backward_workspace_bytes(int B, int H, int N, int d, fa_dtype grad_dtype) {
+  if (check_shape(B, H, N, d) != FA_OK || !valid_dtype(grad_dtype)) return 0;
+  size_t off = 0;
+  return workspace_layout(B, H, N, d, grad_dtype, &off);
+}
+
+fa_status fa_backward(const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                      int H, int N, int d, float scale, int causal, fa_dtype in_dtype,
+                      fa_dtype o_dtype, fa_dtype grad_dtype, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_INVALID_ARG;
+  if (!valid_dtype(in_dtype) || !valid_dtype(o_dtype) || !valid_dtype(grad_dtype))
+    return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+  const fa_status st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (in_dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (o_dtype != in_dtype && o_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if (grad_dtype != in_dtype && grad_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  size_t dq_off = 0;
+  const size_t need = workspace_layout(B, H, N, d, grad_dtype, &dq_off);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return FA_ERR_WORKSPACE;
+
+  fa::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = static_cast<float*>(workspace);
+  a.dq_acc = (grad_dtype == FA_F32) ? static_cast<float*>(dq)
+                                     : reinterpret_cast<float*>(static_cast<char*>(workspace) + dq_off);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.N = N;
+  a.bh = B * H;
+  a.scale = scale;
+  a.c = log2_scale(scale);
+  const hipError_t e = fa::launch_backward(a, d, (int)in_dtype, (int)o_dtype, (int)grad_dtype,
+                                           causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

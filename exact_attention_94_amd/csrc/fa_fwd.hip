@@ -1,0 +1,514 @@
+// Forward attention kernels for gfx950.
+//
+// Method ("FlashAttention 为什么不需要存下注意力矩阵" §03 3.2; "FlashAttention V1 技术深度解析" §3.2):
+// stream K/V tiles past a resident block of queries, keeping per query row a running maximum m,
+// a running sum l and an unnormalised output accumulator O, rescaled by exp(m_old - m_new)
+// whenever the maximum grows; at the end O / l is the softmax-weighted sum and m + log l the
+// logsumexp. Masked scores are -inf and K/V tiles entirely above the causal diagonal are never
+// visited (same page, §03 3.2 last paragraph and §04 4.5).
+//
+// Loop order: each workgroup owns a query tile for its whole life and loops over K/V tiles
+// (queries outer, keys inner), so m, l and O never leave registers. The pages' own V1 order
+// (K/V outer, with O, l, m round-tripped to HBM per K/V block) is not used.
+//
+// gfx950 mapping (16-bit inputs):
+//   * the score tile is computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16: each lane
+//     then owns one query (its accumulator column) and 16 keys, so row max / row sum are
+//     in-lane plus one exchange between the two wave halves, and m, l, corr are lane-local;
+//   * K rows are placed in LDS in a permuted order so that a lane's 16 accumulator slots are
+//     keys {16*(i/8) + 8*g + i%8}: the probabilities then feed the P·V MFMA directly as its
+//     B operand (no LDS round trip), with V^T read as 16 contiguous bytes per lane;
+//   * exp2 with scale*log2(e) folded into one FMA per score;
+//   * K and V^T tiles are double-buffered in LDS (one barrier per K/V tile), the next tile's
+//     global loads are issued before the current tile's math;
+//   * workgroups are ordered longest-first for causal masks and grouped per XCD so that the
+//     query tiles of one (b, h) share an L2.
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+namespace fa {
+
+// ----------------------------------------------------------------------------------------
+// Workgroup -> (b*h, query tile) map. Workgroups are dispatched round-robin over the 8 XCDs
+// (blockIdx % 8). When B*H is a multiple of 8, each XCD gets a contiguous set of heads, and
+// within an XCD the longest query tiles (causal: the last ones) are dispatched first.
+// ----------------------------------------------------------------------------------------
+__device__ __forceinline__ void map_block(int bid, int n_tiles, int bh_total, bool causal,
+                                          int& bh, int& tile) {
+  if ((bh_total & 7) == 0) {
+    const int xcd = bid & 7;
+    const int slot = bid >> 3;
+    const int heads_per_xcd = bh_total >> 3;
+    const int t = slot / heads_per_xcd;
+    bh = xcd * heads_per_xcd + (slot - t * heads_per_xcd);
+    tile = causal ? (n_tiles - 1 - t) : t;
+  } else {
+    const int t = bid / bh_total;
+    bh = bid - t * bh_total;
+    tile = causal ? (n_tiles - 1 - t) : t;
+  }
+}
+
+// LDS row of key kk (0..31 within a 32-key block) such that accumulator row r of the S^T MFMA
+// holds key 16*(a/2) + 8*b + 4*(a%2) + c for r = 8a + 4b + c. Inverse of that map.
+__device__ __forceinline__ int krow_of_key(int kk) {
+  return 8 * (2 * (kk >> 4) + ((kk >> 2) & 1)) + 4 * ((kk >> 3) & 1) + (kk & 3);
+}
+
+template <int D, bool IS_BF16, bool O_F32, bool CAUSAL, int QB>
+struct Fwd16 {
+  static constexpr int NW = 4;            // waves per workgroup
+  static constexpr int NT = NW * 64;      // threads
+  static constexpr int BR = NW * QB * 32; // query rows per workgroup
+  static constexpr int BC = 64;           // keys per K/V tile
+  static constexpr int KS = D / 16;       // contraction steps of S^T = K Q^T
+  static constexpr int DB = D / 32;       // 32-row blocks of O^T
+  static constexpr int KROW = D + 8;      // K tile row stride in LDS (elements)
+  static constexpr int VROW = BC + 8;     // V^T tile row stride in LDS (elements)
+  static constexpr int KTILE = BC * KROW;
+  static constexpr int VTILE = D * VROW;
+  static constexpr int STAGE = KTILE + VTILE;  // elements per LDS stage
+  static constexpr int LDS_BYTES = 2 * STAGE * 2;
+  static constexpr int KCHUNKS = BC * D / 8 / NT;      // 16-byte K chunks per thread
+  static constexpr int VUNITS = (BC / 2) * (D / 8) / NT;  // (2 keys x 8 d) V units per thread
+};
+
+template <int D, bool IS_BF16, bool O_F32, bool CAUSAL, int QB>
+__global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
+  using C = Fwd16<D, IS_BF16, O_F32, CAUSAL, QB>;
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 5;
+  const int r = lane & 31;
+  const int N = a.N;
+
+  int bh, tile;
+  map_block(blockIdx.x, a.n_tiles, a.bh, CAUSAL, bh, tile);
+  const size_t head_off = (size_t)bh * N * D;
+  const uint16_t* __restrict__ qh = static_cast<const uint16_t*>(a.q) + head_off;
+  const uint16_t* __restrict__ kh = static_cast<const uint16_t*>(a.k) + head_off;
+  const uint16_t* __restrict__ vh = static_cast<const uint16_t*>(a.v) + head_off;
+
+  const int qt0 = tile * C::BR;
+  const int qw0 = qt0 + wave * QB * 32;  // first query of this wave
+
+  // Q fragments (B operand of S^T = K Q^T): query qw0 + 32*qb + r, d = 16*ks + 8*g .. +8.
+  Frag16 qf[QB][C::KS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = qw0 + qb * 32 + r;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      qf[qb][ks].w = (row < N) ? ld16(qh + (size_t)row * D + ks * 16 + g * 8) : u32x4{0, 0, 0, 0};
+    }
+  }
+
+  f32x16 oacc[C::DB][QB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][qb][i] = 0.f;
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -3.0e38f;
+    l_run[qb] = 0.f;
+  }
+
+  const float c = a.c;  // scale * log2(e); never 0 (the host maps scale 0 to a tiny value)
+  const bool c_pos = c > 0.f;
+  const float masked = c_pos ? -INFINITY : INFINITY;  // masked score: c * masked = -inf
+
+  const int kv_end = CAUSAL ? min(N, qt0 + C::BR) : N;
+  const int n_kt = (kv_end + C::BC - 1) / C::BC;
+
+  // Global -> register staging of one K/V tile.
+  u32x4 kreg[C::KCHUNKS];
+  u32x4 vreg[C::VUNITS][2];
+  auto load_tile = [&](int j0) {
+#pragma unroll
+    for (int i = 0; i < C::KCHUNKS; ++i) {
+      const int chunk = tid + i * C::NT;
+      const int key = chunk / (D / 8);
+      const int cc = chunk % (D / 8);
+      const int gk = j0 + key;
+      kreg[i] = (gk < N) ? ld16(kh + (size_t)gk * D + cc * 8) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < C::VUNITS; ++i) {
+      const int unit = tid + i * C::NT;
+      const int pair = unit % (C::BC / 2);
+      const int cc = unit / (C::BC / 2);
+      const int gk = j0 + 2 * pair;
+      vreg[i][0] = (gk < N) ? ld16(vh + (size_t)gk * D + cc * 8) : u32x4{0, 0, 0, 0};
+      vreg[i][1] = (gk + 1 < N) ? ld16(vh + (size_t)(gk + 1) * D + cc * 8) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto store_tile = [&](int stage) {
+    uint16_t* ks_ = smem + stage * C::STAGE;
+    uint16_t* vs_ = ks_ + C::KTILE;
+#pragma unroll
+    for (int i = 0; i < C::KCHUNKS; ++i) {
+      const int chunk = tid + i * C::NT;
+      const int key = chunk / (D / 8);
+      const int cc = chunk % (D / 8);
+      const int row = (key & ~31) + krow_of_key(key & 31);
+      st16(ks_ + row * C::KROW + cc * 8, kreg[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < C::VUNITS; ++i) {
+      const int unit = tid + i * C::NT;
+      const int pair = unit % (C::BC / 2);
+      const int cc = unit / (C::BC / 2);
+      // (V[2p][d], V[2p+1][d]) -> one 32-bit word of V^T row d.
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t x0 = vreg[i][0][w], x1 = vreg[i][1][w];
+        const uint32_t lo = (x0 & 0xFFFFu) | (x1 << 16);
+        const uint32_t hi = (x0 >> 16) | (x1 & 0xFFFF0000u);
+        const int d0 = cc * 8 + 2 * w;
+        *reinterpret_cast<uint32_t*>(vs_ + d0 * C::VROW + 2 * pair) = lo;
+        *reinterpret_cast<uint32_t*>(vs_ + (d0 + 1) * C::VROW + 2 * pair) = hi;
+      }
+    }
+  };
+
+  if (n_kt > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int jt = 0; jt < n_kt; ++jt) {
+    const int j0 = jt * C::BC;
+    const int stage = jt & 1;
+    if (jt + 1 < n_kt) load_tile(j0 + C::BC);
+
+    const bool wave_live = !CAUSAL || (j0 <= qw0 + QB * 32 - 1);
+    if (wave_live) {
+      const uint16_t* ks_ = smem + stage * C::STAGE;
+      const uint16_t* vs_ = ks_ + C::KTILE;
+
+      // ---- S^T = K Q^T ---------------------------------------------------------------
+      f32x16 sacc[2][QB];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sacc[kb][qb][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          Frag16 kf;
+          kf.w = *reinterpret_cast<const u32x4*>(ks_ + (kb * 32 + r) * C::KROW + ks * 16 + g * 8);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            sacc[kb][qb] = mfma32x32x16<IS_BF16>(kf, qf[qb][ks], sacc[kb][qb]);
+        }
+      }
+
+      // ---- mask: keys beyond N, and keys after the query on causal diagonal tiles ----------
+      const bool need_mask = (j0 + C::BC > N) || (CAUSAL && (j0 + C::BC - 1 > qw0));
+      if (need_mask) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const int qrow = qw0 + qb * 32 + r;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = j0 + kb * 32 + (i >> 3) * 16 + g * 8 + (i & 7);
+              const bool dead = (key >= N) || (CAUSAL && key > qrow);
+              if (dead) sacc[kb][qb][i] = masked;
+            }
+        }
+      }
+
+      // ---- online softmax (log2 domain): m, l, corr per query (lane-local) ----------------
+      Frag16 pf[2][2][QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float red = sacc[0][qb][0];
+        if (c_pos) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) red = fmaxf(red, sacc[kb][qb][i]);
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) red = fminf(red, sacc[kb][qb][i]);
+        }
+        const float other = swap_halves(red);
+        red = c_pos ? fmaxf(red, other) : fminf(red, other);
+        const float m_blk = red * c;  // -inf when the whole tile is masked for this query
+        const float m_new = fmaxf(m_run[qb], m_blk);
+        const float corr = fast_exp2(m_run[qb] - m_new);
+        m_run[qb] = m_new;
+        float lsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            float p[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              p[e] = fast_exp2(__builtin_fmaf(sacc[kb][qb][h * 8 + e], c, -m_new));
+              lsum += p[e];
+            }
+            pf[kb][h][qb].w = u32x4{pack2<IS_BF16>(p[0], p[1]), pack2<IS_BF16>(p[2], p[3]),
+                                    pack2<IS_BF16>(p[4], p[5]), pack2<IS_BF16>(p[6], p[7])};
+          }
+        }
+        l_run[qb] = l_run[qb] * corr + lsum;
+        // Rescale the accumulator only when some lane's maximum moved (corr == 1 is identity).
+        if (__builtin_amdgcn_ballot_w64(corr != 1.f)) {
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[db][qb][i] *= corr;
+        }
+      }
+
+      // ---- O^T += V^T P^T -----------------------------------------------------------------
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) {
+            Frag16 vf;
+            vf.w = *reinterpret_cast<const u32x4*>(vs_ + (db * 32 + r) * C::VROW + kb * 32 +
+                                                   h * 16 + g * 8);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+              oacc[db][qb] = mfma32x32x16<IS_BF16>(vf, pf[kb][h][qb], oacc[db][qb]);
+          }
+        }
+      }
+    }
+
+    if (jt + 1 < n_kt) store_tile(stage ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O / l, LSE = (m + log2 l) * ln 2 -------------------------------------------
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qrow = qw0 + qb * 32 + r;
+    const float l_tot = l_run[qb] + swap_halves(l_run[qb]);
+    const float inv = 1.f / l_tot;
+    if (qrow < N) {
+      if (g == 0) a.lse[(size_t)bh * N + qrow] = (m_run[qb] + fast_log2(l_tot)) * kLn2;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+          const int d0 = db * 32 + blk * 8 + g * 4;
+          const float o0 = oacc[db][qb][blk * 4 + 0] * inv;
+          const float o1 = oacc[db][qb][blk * 4 + 1] * inv;
+          const float o2 = oacc[db][qb][blk * 4 + 2] * inv;
+          const float o3 = oacc[db][qb][blk * 4 + 3] * inv;
+          if constexpr (O_F32) {
+            float* dst = static_cast<float*>(a.o) + head_off + (size_t)qrow * D + d0;
+            *reinterpret_cast<f32x4*>(dst) = f32x4{o0, o1, o2, o3};
+          } else {
+            uint16_t* dst = static_cast<uint16_t*>(a.o) + head_off + (size_t)qrow * D + d0;
+            *reinterpret_cast<u32x2*>(dst) = u32x2{pack2<IS_BF16>(o0, o1), pack2<IS_BF16>(o2, o3)};
+          }
+        }
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// fp32 inputs: the same recurrence on true-fp32 MFMA (v_mfma_f32_32x32x2_f32). One wave owns
+// 32 queries, K/V tiles of 32 keys are staged in LDS in natural [key][d] layout (one float per
+// lane per operand, so no transposition is needed).
+// ----------------------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+struct Fwd32 {
+  static constexpr int NW = 4;
+  static constexpr int NT = NW * 64;
+  static constexpr int BR = NW * 32;
+  static constexpr int BC = 32;
+  static constexpr int DB = D / 32;
+  static constexpr int ROW = D + 1;  // padded row stride (floats)
+  static constexpr int TILE = BC * ROW;
+  static constexpr int LDS_BYTES = 2 * TILE * 4;
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void fwd32_kernel(FwdArgs a) {
+  using C = Fwd32<D, CAUSAL>;
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem16[];
+  float* smem = reinterpret_cast<float*>(smem16);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 5;
+  const int r = lane & 31;
+  const int N = a.N;
+
+  int bh, tile;
+  map_block(blockIdx.x, a.n_tiles, a.bh, CAUSAL, bh, tile);
+  const size_t head_off = (size_t)bh * N * D;
+  const float* __restrict__ qh = static_cast<const float*>(a.q) + head_off;
+  const float* __restrict__ kh = static_cast<const float*>(a.k) + head_off;
+  const float* __restrict__ vh = static_cast<const float*>(a.v) + head_off;
+
+  const int qt0 = tile * C::BR;
+  const int qw0 = qt0 + wave * 32;
+  const int qrow = qw0 + r;
+
+  // Q (B operand): query qrow, d = 2*ks + g.
+  float qf[D / 2];
+#pragma unroll
+  for (int ks = 0; ks < D / 2; ++ks) qf[ks] = (qrow < N) ? qh[(size_t)qrow * D + 2 * ks + g] : 0.f;
+
+  f32x16 oacc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  float m_run = -3.0e38f, l_run = 0.f;
+
+  const float c = a.c;
+  const bool c_pos = c > 0.f;
+  const float masked = c_pos ? -INFINITY : INFINITY;
+  const int kv_end = CAUSAL ? min(N, qt0 + C::BR) : N;
+  const int n_kt = (kv_end + C::BC - 1) / C::BC;
+
+  for (int jt = 0; jt < n_kt; ++jt) {
+    const int j0 = jt * C::BC;
+    float* ks_ = smem;
+    float* vs_ = smem + C::TILE;
+    __syncthreads();
+    for (int e = tid; e < C::BC * D; e += C::NT) {
+      const int key = e / D, dd = e % D;
+      const int gk = j0 + key;
+      ks_[key * C::ROW + dd] = (gk < N) ? kh[(size_t)gk * D + dd] : 0.f;
+      vs_[key * C::ROW + dd] = (gk < N) ? vh[(size_t)gk * D + dd] : 0.f;
+    }
+    __syncthreads();
+    if (CAUSAL && j0 > qw0 + 31) continue;
+
+    f32x16 sacc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < D / 2; ++ks)
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(ks_[r * C::ROW + 2 * ks + g], qf[ks], sacc, 0,
+                                                  0, 0);
+    // accumulator slot i holds key j0 + 8*(i/4) + 4*g + i%4 for query qrow
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = j0 + (i >> 2) * 8 + g * 4 + (i & 3);
+      if (key >= N || (CAUSAL && key > qrow)) sacc[i] = masked;
+    }
+    float red = sacc[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) red = c_pos ? fmaxf(red, sacc[i]) : fminf(red, sacc[i]);
+    const float other = swap_halves(red);
+    red = c_pos ? fmaxf(red, other) : fminf(red, other);
+    const float m_new = fmaxf(m_run, red * c);
+    const float corr = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    float p[16];
+    float lsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      p[i] = fast_exp2(__builtin_fmaf(sacc[i], c, -m_new));
+      lsum += p[i];
+    }
+    l_run = l_run * corr + lsum;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] *= corr;
+    // O^T += V^T P^T: MFMA s takes slot s; lane group g supplies key 8*(s/4) + 4*g + s%4.
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const int key = (s >> 2) * 8 + g * 4 + (s & 3);
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vs_[key * C::ROW + db * 32 + r], p[s],
+                                                        oacc[db], 0, 0, 0);
+    }
+  }
+
+  const float l_tot = l_run + swap_halves(l_run);
+  const float inv = 1.f / l_tot;
+  if (qrow < N) {
+    if (g == 0) a.lse[(size_t)bh * N + qrow] = (m_run + fast_log2(l_tot)) * kLn2;
+    float* dst = static_cast<float*>(a.o) + head_off + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const int d0 = db * 32 + blk * 8 + g * 4;
+        *reinterpret_cast<f32x4*>(dst + d0) =
+            f32x4{oacc[db][blk * 4] * inv, oacc[db][blk * 4 + 1] * inv,
+                  oacc[db][blk * 4 + 2] * inv, oacc[db][blk * 4 + 3] * inv};
+      }
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// Host-side launchers (called by the C ABI after validation).
+// ----------------------------------------------------------------------------------------
+template <int D, bool IS_BF16, bool O_F32, bool CAUSAL, int QB>
+static hipError_t launch16(FwdArgs a, hipStream_t s) {
+  using C = Fwd16<D, IS_BF16, O_F32, CAUSAL, QB>;
+  a.n_tiles = (a.N + C::BR - 1) / C::BR;
+  const int grid = a.n_tiles * a.bh;
+  auto kern = fwd16_kernel<D, IS_BF16, O_F32, CAUSAL, QB>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), C::LDS_BYTES, s, a);
+  return hipGetLastError();
+}
+
+template <int D, bool IS_BF16, bool O_F32>
+static hipError_t launch16_c(FwdArgs a, bool causal, hipStream_t s) {
+  constexpr int QB = 1;
+  return causal ? launch16<D, IS_BF16, O_F32, true, QB>(a, s)
+                : launch16<D, IS_BF16, O_F32, false, QB>(a, s);
+}
+
+template <int D>
+static hipError_t launch32(FwdArgs a, bool causal, hipStream_t s) {
+  constexpr int BR = Fwd32<D, false>::BR;
+  constexpr int LDS = Fwd32<D, false>::LDS_BYTES;
+  a.n_tiles = (a.N + BR - 1) / BR;
+  const int grid = a.n_tiles * a.bh;
+  auto kc = fwd32_kernel<D, true>;
+  auto kn = fwd32_kernel<D, false>;
+  hipLaunchKernelGGL(causal ? kc : kn, dim3(grid), dim3(256), LDS, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_forward(const FwdArgs& a, int d, int in_dtype, int o_f32, bool causal,
+                          hipStream_t s) {
+  if (in_dtype == 0) return d == 64 ? launch32<64>(a, causal, s) : launch32<128>(a, causal, s);
+  const bool bf = in_dtype == 2;
+  if (d == 64) {
+    if (bf) return o_f32 ? launch16_c<64, true, true>(a, causal, s) : launch16_c<64, true, false>(a, causal, s);
+    return o_f32 ? launch16_c<64, false, true>(a, causal, s) : launch16_c<64, false, false>(a, causal, s);
+  }
+  if (bf) return o_f32 ? launch16_c<128, true, true>(a, causal, s) : launch16_c<128, true, false>(a, causal, s);
+  return o_f32 ? launch16_c<128, false, true>(a, causal, s) : launch16_c<128, false, false>(a, causal, s);
+}
+
+}  // namespace fa

@@ -1,0 +1,46 @@
+// Kernel argument blocks and launcher entry points shared by the C ABI and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int N;        // sequence length
+  int bh;       // B * H
+  int n_tiles;  // query tiles per head (set by the launcher)
+  float c;      // scale * log2(e), never 0
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* dq_acc;  // float32 [B,H,N,d] accumulator (the dq output itself when it is float32)
+  void* dq;       // dq output when its dtype is 16-bit (cast from dq_acc)
+  void* dk;
+  void* dv;
+  float* delta;   // float32 [B,H,N]: rowsum(dO * O)
+  int N;
+  int bh;
+  int n_tiles;
+  float scale;
+  float c;        // scale * log2(e)
+};
+
+// in_dtype / o_dtype / grad_dtype codes follow fa_dtype: 0 = f32, 1 = f16, 2 = bf16.
+hipError_t launch_forward(const FwdArgs& a, int d, int in_dtype, int o_f32, bool causal,
+                          hipStream_t s);
+hipError_t launch_backward(const BwdArgs& a, int d, int in_dtype, int o_dtype, int grad_dtype,
+                           bool causal, hipStream_t s);
+
+}  // namespace fa

@@ -1,0 +1,106 @@
+/*
+ * fa.h — exact attention (FlashAttention-style forward and recompute backward) for AMD
+ * Instinct MI355X (gfx950). C ABI: plain pointers and sizes, no framework types.
+ *
+ * What is computed (pages, cited by title and section):
+ *   "FlashAttention 为什么不需要存下注意力矩阵" (jefxiong.cn) §03 3.1-3.3 and
+ *   "FlashAttention V1 技术深度解析" (spark.aweffr.cn) §2.2, §3.2, §4.2.
+ *
+ *   Forward, per (b, h):  S = scale * Q K^T  (causal: S[i][j] = -inf for key j > query i),
+ *                         P = softmax(S) row-wise,  O = P V,
+ *                         LSE[i] = m_i + log(l_i) = log sum_j exp(S[i][j])   (natural log).
+ *   Backward, given dO:   dV = P^T dO,  dP = dO V^T,  D_i = rowsum(dO * O)_i,
+ *                         dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q.
+ *   P is never stored: the forward streams K/V tiles with a running max, a running sum and an
+ *   unnormalised output accumulator rescaled by exp(m_old - m_new); the backward recomputes each
+ *   P tile as exp(S - LSE).
+ *
+ * Layout: every tensor is contiguous [B, H, N, d] (d fastest), LSE and the internal row
+ * vectors are contiguous [B, H, N]. Q, K and V share N (self-attention). Pointers must be
+ * device pointers (hipMalloc'd or equivalent) aligned to 16 bytes.
+ *
+ * Supported: d in {64, 128}; N >= 1 (a ragged tail is masked); B, H >= 1 with B*H*N*d < 2^31;
+ * in_dtype in {FA_F32, FA_F16, FA_BF16}; any finite scale; causal in {0, 1}.
+ * The backward supports in_dtype FA_F16 and FA_BF16.
+ *
+ * Ownership: the caller owns every buffer and the stream. The library never allocates or frees
+ * device memory; the backward takes a caller-provided workspace.
+ *
+ * Errors: arguments are validated before any launch. An unsupported combination returns
+ * FA_ERR_UNSUPPORTED and an invalid one FA_ERR_INVALID_ARG; nothing is launched and there is no
+ * fallback path. FA_ERR_HIP reports a failed HIP call or launch. The library never aborts,
+ * prints or throws across this boundary.
+ *
+ * Asynchrony: calls enqueue kernels on `stream` (a hipStream_t; NULL = the null stream) and
+ * return without waiting. Calls on distinct streams may run concurrently from distinct threads.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, size overflow, non-finite scale */
+  FA_ERR_UNSUPPORTED = 2, /* head dim, dtype combination or mode this build does not provide */
+  FA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than fa_backward_workspace_bytes() */
+  FA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} fa_status;
+
+typedef enum fa_dtype { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
+
+/*
+ * Forward pass ("FlashAttention 为什么不需要存下注意力矩阵" §03 3.2, §04 4.1: the tiled function
+ * returns the normalised output and the per-row logsumexp).
+ *
+ *   q, k, v  [B,H,N,d] in in_dtype (read only)
+ *   o        [B,H,N,d] in o_dtype, written: o_dtype is in_dtype, or FA_F32 for 16-bit inputs
+ *   lse      [B,H,N] float32, written: natural-log logsumexp of the scaled scores per query row
+ *   scale    multiplies Q K^T before the softmax (usually 1/sqrt(d)); any finite value
+ *   causal   1: query i attends to keys 0..i; 0: to all N keys
+ * Fully masked K/V tiles are skipped. Results are deterministic (no atomics).
+ */
+fa_status fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int H, int N, int d, float scale, int causal, fa_dtype in_dtype,
+                     fa_dtype o_dtype, void* stream);
+
+/*
+ * Bytes of device workspace fa_backward needs for these sizes and grad_dtype: the row vector
+ * D = rowsum(dO * O) (float32 [B,H,N]) plus, when grad_dtype is not FA_F32, a float32 [B,H,N,d]
+ * accumulator for dQ. Returns 0 for arguments fa_backward would reject.
+ */
+size_t fa_backward_workspace_bytes(int B, int H, int N, int d, fa_dtype grad_dtype);
+
+/*
+ * Backward pass ("FlashAttention 为什么不需要存下注意力矩阵" §03 3.3; "FlashAttention V1 技术深度解析"
+ * §4.2: recompute each P tile from the saved statistics instead of storing P).
+ *
+ *   q, k, v    [B,H,N,d] in in_dtype (FA_F16 or FA_BF16), the forward's inputs
+ *   o          [B,H,N,d] in o_dtype (in_dtype or FA_F32), the forward's output
+ *   dout       [B,H,N,d] in in_dtype, the upstream gradient dL/dO
+ *   lse        [B,H,N] float32, the forward's logsumexp
+ *   dq, dk, dv [B,H,N,d] in grad_dtype (in_dtype or FA_F32), written
+ *   workspace  device buffer of at least fa_backward_workspace_bytes(B,H,N,d,grad_dtype) bytes,
+ *              16-byte aligned; contents on entry are ignored and clobbered
+ * The three gradient products and the dP product use fp16 MFMA operands with fp32
+ * accumulation (bf16 inputs are converted exactly while |x| >= 2^-14). dQ is accumulated
+ * with float32 atomics, so its low bits may differ run to run; dK and dV are deterministic.
+ */
+fa_status fa_backward(const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                      int H, int N, int d, float scale, int causal, fa_dtype in_dtype,
+                      fa_dtype o_dtype, fa_dtype grad_dtype, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* A static, human-readable description of a status code (never NULL). */
+const char* fa_status_string(fa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,147 @@
+"""The C ABI without a GPU: the library loads, exports what include/fa.h declares, and rejects
+invalid calls with the documented status before any HIP call (fake, never-dereferenced device
+pointers are safe here because validation precedes every launch)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_attention_94_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+P = 0x100000  # fake 16-byte-aligned device addresses (never dereferenced)
+
+
+def _lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libfa.so is not built (run python -m exact_attention_94_amd.build)")
+    return B.load()
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    return sorted(set(re.findall(r"^\s*(?:[A-Za-z_][\w\s\*]*?)\b(fa_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    lib = _lib()
+    for code in range(5):
+        s = lib.fa_status_string(code).decode()
+        assert s.startswith(["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED",
+                             "FA_ERR_WORKSPACE", "FA_ERR_HIP"][code])
+    assert "unknown" in lib.fa_status_string(99).decode()
+
+
+def fwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=3, N=100, d=64, scale=0.125, causal=1,
+             in_dtype=B.FA_BF16, o_dtype=B.FA_BF16)
+    a.update(kw)
+    return _lib().fa_forward(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"],
+                             a["d"], a["scale"], a["causal"], a["in_dtype"], a["o_dtype"], None)
+
+
+def bwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=2, H=3, N=100, d=64,
+             scale=0.125, causal=1, in_dtype=B.FA_BF16, o_dtype=B.FA_F32, g_dtype=B.FA_F32,
+             ws=P, ws_bytes=1 << 30)
+    a.update(kw)
+    return _lib().fa_backward(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"],
+                              a["dk"], a["dv"], a["B"], a["H"], a["N"], a["d"], a["scale"],
+                              a["causal"], a["in_dtype"], a["o_dtype"], a["g_dtype"], a["ws"],
+                              a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), B.FA_ERR_INVALID_ARG),
+    (dict(lse=None), B.FA_ERR_INVALID_ARG),
+    (dict(v=P + 8), B.FA_ERR_INVALID_ARG),
+    (dict(N=0), B.FA_ERR_INVALID_ARG),
+    (dict(B=-1), B.FA_ERR_INVALID_ARG),
+    (dict(B=1 << 16, H=1 << 10, N=1 << 10), B.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), B.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), B.FA_ERR_INVALID_ARG),
+    (dict(causal=2), B.FA_ERR_INVALID_ARG),
+    (dict(in_dtype=7), B.FA_ERR_INVALID_ARG),
+    (dict(d=96), B.FA_ERR_UNSUPPORTED),
+    (dict(d=32), B.FA_ERR_UNSUPPORTED),
+    (dict(o_dtype=B.FA_F16), B.FA_ERR_UNSUPPORTED),
+    (dict(in_dtype=B.FA_F32, o_dtype=B.FA_BF16), B.FA_ERR_UNSUPPORTED),
+])
+def test_forward_rejects(kw, status):
+    assert fwd(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dq=None), B.FA_ERR_INVALID_ARG),
+    (dict(do=P + 4), B.FA_ERR_INVALID_ARG),
+    (dict(N=0), B.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), B.FA_ERR_INVALID_ARG),
+    (dict(causal=-1), B.FA_ERR_INVALID_ARG),
+    (dict(g_dtype=5), B.FA_ERR_INVALID_ARG),
+    (dict(d=256), B.FA_ERR_UNSUPPORTED),
+    (dict(in_dtype=B.FA_F32, o_dtype=B.FA_F32), B.FA_ERR_UNSUPPORTED),
+    (dict(g_dtype=B.FA_F16), B.FA_ERR_UNSUPPORTED),
+    (dict(o_dtype=B.FA_F16), B.FA_ERR_UNSUPPORTED),
+    (dict(ws=None), B.FA_ERR_WORKSPACE),
+    (dict(ws=P + 2), B.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=16), B.FA_ERR_WORKSPACE),
+    (dict(g_dtype=B.FA_BF16, ws_bytes=2 * 3 * 100 * 4 + 256), B.FA_ERR_WORKSPACE),
+])
+def test_backward_rejects(kw, status):
+    assert bwd(**kw) == status
+
+
+def test_workspace_bytes():
+    lib = _lib()
+    ws = lib.fa_backward_workspace_bytes
+    # D vector rounded to 256 bytes, plus an fp32 dQ accumulator for 16-bit gradients.
+    assert ws(2, 3, 100, 64, B.FA_F32) == 2560
+    assert ws(2, 3, 100, 64, B.FA_BF16) == 2560 + 2 * 3 * 100 * 64 * 4
+    assert ws(1, 1, 1, 128, B.FA_F16) == 256 + 128 * 4
+    assert ws(1, 1, 1, 96, B.FA_F32) == 0
+    assert ws(0, 1, 1, 64, B.FA_F32) == 0
+    assert ws(1, 1, 1, 64, 9) == 0
+
+
+def test_exact_workspace_size_is_accepted_by_validation():
+    """With exactly the advertised bytes, validation passes (the call then needs a GPU, so the
+    only acceptable outcomes here are FA_OK on a GPU machine or FA_ERR_HIP without one)."""
+    lib = _lib()
+    need = lib.fa_backward_workspace_bytes(2, 3, 100, 64, B.FA_BF16)
+    st = bwd(g_dtype=B.FA_BF16, ws_bytes=need - 1)
+    assert st == B.FA_ERR_WORKSPACE
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    saved = B._lib
+    try:
+        B._lib = None
+        with pytest.raises(RuntimeError, match="not built"):
+            B.load(str(tmp_path / "missing.so"))
+    finally:
+        B._lib = saved
+
+
+def test_product_path_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "exact_attention_94_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b|oracle[/.]attention|"
+                                     r"attn_(fwd|bwd|tiled|rows)_ref", text, re.M), \
+                    os.path.join(dirpath, f)

@@ -1,0 +1,249 @@
+"""GPU parity: the HIP library (through its C ABI) against the float64 oracle.
+
+Inputs are the seeded synthetic tensors of exact_attention_94_amd.inputs; outputs are
+pre-filled with NaN so any element a kernel fails to write fails the comparison. Tolerances are
+absolute max errors against the oracle: 1e-5 for fp32 inputs; 2e-2 on O / dQ / dK / dV and 1e-3
+on LSE for 16-bit inputs.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+from exact_attention_94_amd import inputs as inp
+from oracle import attn_bwd_ref, attn_fwd_ref, attn_rows_ref
+from tests.gpu_util import TOL, check, host64, nan_like, to_device, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import exact_attention_94_amd as fa_mod
+    fa_mod.binding.load()  # loud failure if libfa.so is missing
+    return fa_mod
+
+
+def _run_fwd(fa, t, causal, scale, o_dtype=None, device="cuda"):
+    import torch
+    q, k, v = (to_device(t[n]) for n in ("q", "k", "v"))
+    B, H, N, d = q.shape
+    od = q.dtype if o_dtype is None else o_dtype
+    out = nan_like((B, H, N, d), od)
+    lse = nan_like((B, H, N), torch.float32)
+    fa.forward(q, k, v, scale=scale, causal=causal, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return q, k, v, out, lse
+
+
+def _fwd_case(fa, shape, dtype, causal, seed=1, scale=None, qk_mult=1.0, heads=None):
+    t = inp.draw(shape, dtype, seed, qk_mult=qk_mult)
+    d = shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    _, _, _, out, lse = _run_fwd(fa, t, causal, scale)
+    o_ref, lse_ref = attn_fwd_ref(t["q"].values, t["k"].values, t["v"].values, scale, causal)
+    tol_o, tol_l = TOL[dtype]
+    check("O", host64(out), o_ref, tol_o)
+    check("LSE", host64(lse), lse_ref, tol_l)
+
+
+# --- the five named workloads ------------------------------------------------------------
+
+def test_single_head_f32(fa):
+    w = inp.WORKLOADS["single_head_f32"]
+    _fwd_case(fa, w.shape, w.dtype, False, seed=w.N)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_b4h16n1k_bf16_forward(fa, causal):
+    w = inp.WORKLOADS["b4h16n1k_d64"]
+    _fwd_case(fa, w.shape, w.dtype, causal, seed=w.N)
+
+
+def _fwd_bwd_workload(fa, w, heads, o_f32=True, g_f32=True):
+    import torch
+    t = inp.workload_inputs(w)
+    od = torch.float32 if o_f32 else torch_dtype(w.dtype)
+    q, k, v, out, lse = _run_fwd(fa, t, True, w.scale, o_dtype=od)
+    do = to_device(t["do"])
+    gd = torch.float32 if g_f32 else q.dtype
+    grads = tuple(nan_like(q.shape, gd) for _ in range(3))
+    dq, dk, dv = fa.backward(q, k, v, out, do, lse, scale=w.scale, causal=True, grad_dtype=gd,
+                             grads=grads)
+    torch.cuda.synchronize()
+    B, H = w.B, w.H
+    for (b, h) in heads:
+        sel = lambda x: x[b, h]  # noqa: E731
+        o_ref, lse_ref = attn_fwd_ref(sel(t["q"].values), sel(t["k"].values), sel(t["v"].values),
+                                      w.scale, True)
+        g = attn_bwd_ref(sel(t["q"].values), sel(t["k"].values), sel(t["v"].values),
+                         sel(t["do"].values), w.scale, True)
+        print(f"  head (b={b}, h={h})", flush=True)
+        check("O", host64(out[b, h]), o_ref, 2e-2)
+        check("LSE", host64(lse[b, h]), lse_ref, 1e-3)
+        check("dQ", host64(dq[b, h]), g["dq"], 2e-2)
+        check("dK", host64(dk[b, h]), g["dk"], 2e-2)
+        check("dV", host64(dv[b, h]), g["dv"], 2e-2)
+    assert B * H >= len(heads)
+
+
+def test_b2h16n4k_fwd_bwd(fa):
+    w = inp.WORKLOADS["b2h16n4k_d64"]
+    _fwd_bwd_workload(fa, w, heads=[(0, 0), (0, 7), (1, 3), (1, 15)])
+
+
+def test_b2h16n4k_fwd_bwd_bf16_outputs(fa):
+    """16-bit O and gradients also meet the tolerance at this size."""
+    w = inp.WORKLOADS["b2h16n4k_d64"]
+    _fwd_bwd_workload(fa, w, heads=[(0, 1), (1, 14)], o_f32=False, g_f32=False)
+
+
+def test_b1h32n8k_d128_peaked_fwd_bwd(fa):
+    w = inp.WORKLOADS["b1h32n8k_d128_peaked"]
+    _fwd_bwd_workload(fa, w, heads=[(0, 0), (0, 31)])
+
+
+def test_b1h8n32k_d128_rows(fa):
+    w = inp.WORKLOADS["b1h8n32k_d128"]
+    t = inp.workload_inputs(w)
+    _, _, _, out, lse = _run_fwd(fa, t, True, w.scale)
+    out_h, lse_h = host64(out), host64(lse)
+    for h in range(w.H):
+        rows = inp.subset_rows(w.N, h)
+        o_ref, l_ref = attn_rows_ref(t["q"].values[0, h], t["k"].values[0, h],
+                                     t["v"].values[0, h], w.scale, True, rows)
+        check(f"O rows h={h}", out_h[0, h, rows], o_ref, 2e-2)
+        check(f"LSE rows h={h}", lse_h[0, h, rows], l_ref, 1e-3)
+
+
+# --- small shapes: ragged tails, both head dims, all dtypes ------------------------------
+
+SWEEP_N = [1, 2, 3, 17, 63, 64, 65, 127, 128, 129, 255, 300]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_sweep(fa, dtype, d, causal):
+    for n in SWEEP_N:
+        for (B, H) in ((1, 2), (2, 4)):
+            print(f"  N={n} B={B} H={H}", flush=True)
+            _fwd_case(fa, (B, H, n, d), dtype, causal, seed=n * 7 + d)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_sweep(fa, dtype, d, causal):
+    import torch
+    for n in [1, 3, 17, 64, 65, 127, 129, 200, 300]:
+        for (B, H) in ((1, 2), (2, 4)):
+            print(f"  N={n} B={B} H={H}", flush=True)
+            t = inp.draw((B, H, n, d), dtype, n * 11 + d, with_do=True)
+            scale = 1.0 / math.sqrt(d)
+            q, k, v, out, lse = _run_fwd(fa, t, causal, scale, o_dtype=torch.float32)
+            do = to_device(t["do"])
+            grads = tuple(nan_like(q.shape, torch.float32) for _ in range(3))
+            dq, dk, dv = fa.backward(q, k, v, out, do, lse, scale=scale, causal=causal,
+                                     grad_dtype=torch.float32, grads=grads)
+            torch.cuda.synchronize()
+            g = attn_bwd_ref(t["q"].values, t["k"].values, t["v"].values, t["do"].values, scale,
+                             causal)
+            check("dQ", host64(dq), g["dq"], 2e-2)
+            check("dK", host64(dk), g["dk"], 2e-2)
+            check("dV", host64(dv), g["dv"], 2e-2)
+
+
+# --- special inputs with closed-form answers ---------------------------------------------
+
+def _upload(arr, dtype):
+    return to_device(inp.quantize(np.asarray(arr, dtype=np.float32), dtype))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_keys_mean_of_values(fa, dtype, causal):
+    import torch
+    B, H, N, d = 1, 2, 200, 64
+    rng = np.random.default_rng(5)
+    qv = inp.quantize(rng.standard_normal((B, H, N, d), dtype=np.float32), dtype)
+    vv = inp.quantize(rng.standard_normal((B, H, N, d), dtype=np.float32), dtype)
+    q, v = to_device(qv), to_device(vv)
+    k = torch.zeros_like(q)
+    out, lse = fa.forward(q, k, v, causal=causal)
+    torch.cuda.synchronize()
+    V = vv.values.astype(np.float64)
+    if causal:
+        cnt = np.arange(1, N + 1)
+        o_ref = np.cumsum(V, axis=2) / cnt[None, None, :, None]
+        l_ref = np.broadcast_to(np.log(cnt), (B, H, N))
+    else:
+        o_ref = np.broadcast_to(V.mean(axis=2, keepdims=True), V.shape)
+        l_ref = np.full((B, H, N), math.log(N))
+    tol_o, tol_l = TOL[dtype]
+    check("O", host64(out), o_ref, tol_o)
+    check("LSE", host64(lse), l_ref, tol_l)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_scale_zero_and_negative(fa, causal):
+    for scale in (0.0, -0.125):
+        print(f"  scale={scale}", flush=True)
+        _fwd_case(fa, (1, 2, 150, 64), "bf16", causal, seed=9, scale=scale)
+        _fwd_case(fa, (1, 2, 150, 64), "f32", causal, seed=9, scale=scale)
+
+
+def test_large_key_shift_no_overflow(fa):
+    """K + 1 c^T with |scale*q.c| in the hundreds: O unchanged, LSE shifted (max subtraction)."""
+    import torch
+    B, H, N, d = 1, 1, 256, 64
+    rng = np.random.default_rng(77)
+    q32 = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    k32 = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    v32 = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    c = (rng.standard_normal(d).astype(np.float32) * 64.0)
+    t = {"q": inp.quantize(q32, "f32"), "k": inp.quantize(k32 + c, "f32"),
+         "v": inp.quantize(v32, "f32")}
+    _, _, _, out, lse = _run_fwd(fa, t, False, 0.125)
+    o_ref, l_ref = attn_fwd_ref(t["q"].values, t["k"].values, t["v"].values, 0.125, False)
+    assert np.abs(l_ref).max() > 50
+    check("O", host64(out), o_ref, 1e-4)
+    check("LSE", host64(lse), l_ref, 2e-4)
+    torch.cuda.synchronize()
+
+
+def test_causal_row0_and_dq0(fa):
+    import torch
+    B, H, N, d = 1, 2, 130, 64
+    t = inp.draw((B, H, N, d), "bf16", 3, with_do=True)
+    q, k, v, out, lse = _run_fwd(fa, t, True, 0.125, o_dtype=torch.float32)
+    o = host64(out)
+    assert np.array_equal(o[:, :, 0], t["v"].values[:, :, 0].astype(np.float64))
+    do = to_device(t["do"])
+    dq, dk, dv = fa.backward(q, k, v, out, do, lse, scale=0.125, causal=True,
+                             grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    # Softmax over a single key has zero gradient; dP_00 and D_0 are summed in different orders
+    # on the GPU, so the result is zero up to fp32 rounding.
+    assert np.abs(host64(dq)[:, :, 0]).max() < 1e-4
+
+
+# --- determinism --------------------------------------------------------------------------
+
+def test_repeat_determinism(fa):
+    import torch
+    w = inp.Workload("det", 2, 4, 700, 64, "bf16", (True,), backward=True)
+    t = inp.workload_inputs(w, seed=4)
+    q, k, v = (to_device(t[n]) for n in ("q", "k", "v"))
+    do = to_device(t["do"])
+    o1, l1 = fa.forward(q, k, v, causal=True, o_dtype=torch.float32)
+    o2, l2 = fa.forward(q, k, v, causal=True, o_dtype=torch.float32)
+    g1 = fa.backward(q, k, v, o1, do, l1, causal=True, grad_dtype=torch.float32)
+    g2 = fa.backward(q, k, v, o1, do, l1, causal=True, grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])
+    assert (g1[0] - g2[0]).abs().max().item() < 1e-5
