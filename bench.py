@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = fa_forward + fa_backward over the headline workload (B=2, H=16, N=4096, d=64, causal,
+bf16 inputs; O and the gradients in fp32), inputs resident in HBM before timing starts.
+Prints ONE JSON line with the step throughput, the forward and backward TFLOP/s and their share of
+the MI355X dense bf16/fp16 MFMA peak, a roofline record for the dominant kernel (the main backward
+kernel, timed alone with HIP events that the library records around its launch), and the float64
+CPU oracle timed on a bounded sample of the same workload on this host.
+
+FLOP convention: forward 4*B*H*N^2*d, halved when causal; backward 2.5x the forward.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+HBM_PEAK_GBS = 8000.0
+METRIC = "attention fwd/bwd TFLOP/s + % bf16 MFMA peak (B2 H16 N4096 d64 causal)"
+WORKLOAD = "b2h16n4k_d64"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_main_b2h16n4k_d64_traffic.txt")
+BWD_SOURCE = os.path.join(ROOT, "exact_attention_94_amd", "csrc", "fa_bwd.hip")
+
+
+def flops(w):
+    fwd = 4.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if True in w.causal else 1.0)
+    return fwd, 2.5 * fwd
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime already loaded by torch."""
+
+    def __init__(self):
+        self.rt = ctypes.CDLL("libamdhip64.so.7")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.rt.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        if self.rt.hipEventCreate(ctypes.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return ev.value
+
+    def record(self, ev, stream):
+        if self.rt.hipEventRecord(ev, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        self.rt.hipEventSynchronize(b)
+        if self.rt.hipEventElapsedTime(ctypes.byref(out), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+    def destroy(self, ev):
+        self.rt.hipEventDestroy(ev)
+
+
+def source_digest(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the main backward kernel from the committed rocprofv3 counter
+    summary, or None when it is absent or was taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE, encoding="utf-8").read()
+    m_src = re.search(r"^kernel_source_sha256_16:\s*(\w+)", text, re.M)
+    m_tot = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not (m_src and m_tot) or m_src.group(1) != source_digest(BWD_SOURCE):
+        return None
+    return float(m_tot.group(1))
+
+
+def cpu_baseline(w, t, heads=32):
+    """Float64 oracle (forward + backward) on `heads` of the workload's heads, this host's cores."""
+    from oracle import attn_bwd_ref, attn_fwd_ref
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
+    except Exception:
+        threads = None
+    f_fwd, f_bwd = flops(w)
+    per_head = (f_fwd + f_bwd) / (w.B * w.H)
+    t0 = time.perf_counter()
+    for hh in range(heads):
+        b, h = divmod(hh, w.H)
+        sel = lambda x: x[b, h]  # noqa: E731
+        attn_fwd_ref(sel(t["q"].values), sel(t["k"].values), sel(t["v"].values), w.scale, True)
+        attn_bwd_ref(sel(t["q"].values), sel(t["k"].values), sel(t["v"].values),
+                     sel(t["do"].values), w.scale, True)
+    dt = time.perf_counter() - t0
+    return {"value": round(per_head * heads / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": threads or os.cpu_count(), "kind": "oracle",
+            "sample": f"float64 NumPy oracle, forward+backward of {heads} of the {w.B * w.H} heads "
+                      f"(N={w.N}, d={w.d}, causal), {dt:.1f} s; nominal FLOPs of those heads "
+                      f"divided by wall time"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=32)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the attention path is single-GPU; see the sharding notes in DESIGN.md)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import exact_attention_94_amd as fa
+    from exact_attention_94_amd import inputs as inp
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    fa.binding.load()
+    dev = torch.device("cuda:0")
+
+    if args.copy_mib:
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": n * 4, "launches": 3}))
+        return 0
+
+    w = inp.WORKLOADS[WORKLOAD]
+    t = inp.workload_inputs(w)
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x.bits).view(np.int16)).view(
+            torch.bfloat16).to(dev)
+
+    q, k, v, do = (up(t[n]) for n in ("q", "k", "v", "do"))
+    shape = (w.B, w.H, w.N, w.d)
+    o = torch.empty(shape, dtype=torch.float32, device=dev)
+    lse = torch.empty(shape[:3], dtype=torch.float32, device=dev)
+    grads = tuple(torch.empty(shape, dtype=torch.float32, device=dev) for _ in range(3))
+    ws = torch.empty(fa.workspace_bytes(*shape, fa.FA_F32), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def step():
+        fa.forward(q, k, v, scale=w.scale, causal=True, out=o, lse=lse)
+        fa.backward(q, k, v, o, do, lse, scale=w.scale, causal=True, grad_dtype=torch.float32,
+                    workspace=ws, grads=grads)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = HipEvents()
+    K = args.steps
+    e_start, e_end = ev.create(), ev.create()
+    ef0 = [ev.create() for _ in range(K)]
+    ef1 = [ev.create() for _ in range(K)]
+    eb0 = [ev.create() for _ in range(K)]
+    eb1 = [ev.create() for _ in range(K)]
+    eb2 = [ev.create() for _ in range(K)]
+
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    ev.record(e_start, stream)
+    for i in range(K):
+        ev.record(ef0[i], stream)
+        fa.forward(q, k, v, scale=w.scale, causal=True, out=o, lse=lse)
+        ev.record(ef1[i], stream)
+        fa.binding.profile_backward_main(eb0[i], eb1[i])
+        fa.backward(q, k, v, o, do, lse, scale=w.scale, causal=True, grad_dtype=torch.float32,
+                    workspace=ws, grads=grads)
+        ev.record(eb2[i], stream)
+    fa.binding.profile_backward_main(None, None)
+    ev.record(e_end, stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+
+    step_ms = ev.ms(e_start, e_end) / K
+    fwd_ms = sum(ev.ms(ef0[i], ef1[i]) for i in range(K)) / K
+    bwd_ms = sum(ev.ms(ef1[i], eb2[i]) for i in range(K)) / K
+    main_ms = sum(ev.ms(eb0[i], eb1[i]) for i in range(K)) / K
+    for e in [e_start, e_end] + ef0 + ef1 + eb0 + eb1 + eb2:
+        ev.destroy(e)
+    assert torch.isfinite(o).all() and all(torch.isfinite(g).all() for g in grads)
+
+    f_fwd, f_bwd = flops(w)
+    tf = lambda f, ms: f / (ms * 1e-3) / 1e12  # noqa: E731
+    value = tf(f_fwd + f_bwd, step_ms)
+    main_tf = tf(f_bwd, main_ms)
+    traffic = measured_traffic()
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "B=2 H=16 N=4096 d=64 causal, bf16 inputs, forward+backward",
+                   "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": True,
+                   "o_dtype": "f32", "grad_dtype": "f32", "bwd_mfma_operands": "f16",
+                   "seed": w.N, "parallelism": "single GPU"},
+        "fwd_tflops": round(tf(f_fwd, fwd_ms), 2),
+        "fwd_pct_peak": round(100 * tf(f_fwd, fwd_ms) / PEAK_BF16_TFLOPS, 2),
+        "fwd_ms": round(fwd_ms, 4),
+        "bwd_tflops": round(tf(f_bwd, bwd_ms), 2),
+        "bwd_pct_peak": round(100 * tf(f_bwd, bwd_ms) / PEAK_BF16_TFLOPS, 2),
+        "bwd_ms": round(bwd_ms, 4),
+        "step_pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "host_wall_ms_per_step": round(1e3 * t_wall / K, 4),
+        "roofline": {
+            "kernel": "bwd_main_kernel<64, bf16, f32 grads, causal>",
+            "bound": "mfma",
+            "achieved": round(main_tf, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(main_tf / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel_ms": round(main_ms, 4),
+            "flops_per_launch": f_bwd,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, t, heads=args.cpu_heads)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -18,7 +18,8 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = ra
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_forward", "fa_backward", "fa_backward_workspace_bytes", "fa_status_string")
+EXPORTS = ("fa_forward", "fa_backward", "fa_backward_workspace_bytes", "fa_profile_backward_main",
+           "fa_status_string")
 
 _lib = None
 
@@ -48,6 +49,8 @@ def load(path=LIB_PATH):
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, i,
                                 vp, sz, vp]
     lib.fa_backward.restype = i
+    lib.fa_profile_backward_main.argtypes = [vp, vp]
+    lib.fa_profile_backward_main.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -113,6 +116,14 @@ def forward(q, k, v, scale=None, causal=False, o_dtype=None, out=None, lse=None)
     if st != FA_OK:
         raise FAError(st, "fa_forward")
     return out, lse
+
+
+def profile_backward_main(before, after):
+    """Ask this thread's fa_backward calls to record two hipEvent_t handles (ints) around the main
+    backward kernel; (None, None) stops."""
+    st = load().fa_profile_backward_main(before, after)
+    if st != FA_OK:
+        raise FAError(st, "fa_profile_backward_main")
 
 
 def workspace_bytes(B, H, N, d, grad_dtype_code):

@@ -31,6 +31,10 @@ float log2_scale(float scale) {
   return c == 0.f ? 1e-30f : c;
 }
 
+// Events the calling thread asked fa_backward to record around its main kernel.
+thread_local hipEvent_t t_prof_before = nullptr;
+thread_local hipEvent_t t_prof_after = nullptr;
+
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 size_t workspace_layout(int B, int H, int N, int d, fa_dtype grad_dtype, size_t* dq_off) {
@@ -129,8 +133,16 @@ fa_status fa_backward(const void* q, const void* k, const void* v, const void* o
   a.scale = scale;
   a.c = log2_scale(scale);
   const hipError_t e = fa::launch_backward(a, d, (int)in_dtype, (int)o_dtype, (int)grad_dtype,
-                                           causal != 0, static_cast<hipStream_t>(stream));
+                                           causal != 0, static_cast<hipStream_t>(stream),
+                                           t_prof_before, t_prof_after);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_profile_backward_main(void* before, void* after) {
+  if ((before == nullptr) != (after == nullptr)) return FA_ERR_INVALID_ARG;
+  t_prof_before = static_cast<hipEvent_t>(before);
+  t_prof_after = static_cast<hipEvent_t>(after);
+  return FA_OK;
 }
 
 }  // extern "C"

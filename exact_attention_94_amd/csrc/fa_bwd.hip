@@ -433,14 +433,16 @@ static hipError_t launch_main(BwdArgs a, hipStream_t s) {
 
 template <int D, bool IS_BF16>
 static hipError_t launch_all(const BwdArgs& a, bool o_f32, bool g_f32, bool causal,
-                             hipStream_t s) {
+                             hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after) {
   hipError_t e = launch_pre<D, IS_BF16>(a, o_f32, s);
   if (e != hipSuccess) return e;
+  if (ev_before && (e = hipEventRecord(ev_before, s)) != hipSuccess) return e;
   if (g_f32)
     e = causal ? launch_main<D, IS_BF16, true, true>(a, s) : launch_main<D, IS_BF16, true, false>(a, s);
   else
     e = causal ? launch_main<D, IS_BF16, false, true>(a, s) : launch_main<D, IS_BF16, false, false>(a, s);
   if (e != hipSuccess) return e;
+  if (ev_after && (e = hipEventRecord(ev_after, s)) != hipSuccess) return e;
   if (!g_f32) {
     const long long n8 = (long long)a.bh * a.N * D / 8;
     hipLaunchKernelGGL((dq_cast_kernel<IS_BF16>), dim3((unsigned)((n8 + 255) / 256)), dim3(256),
@@ -451,14 +453,14 @@ static hipError_t launch_all(const BwdArgs& a, bool o_f32, bool g_f32, bool caus
 }
 
 hipError_t launch_backward(const BwdArgs& a, int d, int in_dtype, int o_dtype, int grad_dtype,
-                           bool causal, hipStream_t s) {
+                           bool causal, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after) {
   const bool bf = in_dtype == 2;
   const bool o_f32 = o_dtype == 0;
   const bool g_f32 = grad_dtype == 0;
-  if (d == 64) return bf ? launch_all<64, true>(a, o_f32, g_f32, causal, s)
-                         : launch_all<64, false>(a, o_f32, g_f32, causal, s);
-  return bf ? launch_all<128, true>(a, o_f32, g_f32, causal, s)
-            : launch_all<128, false>(a, o_f32, g_f32, causal, s);
+  if (d == 64) return bf ? launch_all<64, true>(a, o_f32, g_f32, causal, s, ev_before, ev_after)
+                         : launch_all<64, false>(a, o_f32, g_f32, causal, s, ev_before, ev_after);
+  return bf ? launch_all<128, true>(a, o_f32, g_f32, causal, s, ev_before, ev_after)
+            : launch_all<128, false>(a, o_f32, g_f32, causal, s, ev_before, ev_after);
 }
 
 }  // namespace fa

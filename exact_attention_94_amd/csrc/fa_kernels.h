@@ -40,7 +40,8 @@ struct BwdArgs {
 // in_dtype / o_dtype / grad_dtype codes follow fa_dtype: 0 = f32, 1 = f16, 2 = bf16.
 hipError_t launch_forward(const FwdArgs& a, int d, int in_dtype, int o_f32, bool causal,
                           hipStream_t s);
+// ev_before / ev_after (may be null): recorded on `s` around the main backward kernel.
 hipError_t launch_backward(const BwdArgs& a, int d, int in_dtype, int o_dtype, int grad_dtype,
-                           bool causal, hipStream_t s);
+                           bool causal, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after);
 
 }  // namespace fa

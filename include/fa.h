@@ -96,6 +96,15 @@ fa_status fa_backward(const void* q, const void* k, const void* v, const void* o
                       fa_dtype o_dtype, fa_dtype grad_dtype, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/*
+ * Profiling aid with no effect on results: after this call, every fa_backward call made by the
+ * calling thread records `before` on its stream immediately before the main backward kernel is
+ * launched and `after` immediately after it, so the caller can time that kernel alone with
+ * hipEventElapsedTime. Both are hipEvent_t handles owned by the caller. Pass NULL, NULL to stop.
+ * Returns FA_ERR_INVALID_ARG if exactly one of them is NULL, FA_OK otherwise.
+ */
+fa_status fa_profile_backward_main(void* before, void* after);
+
 /* A static, human-readable description of a status code (never NULL). */
 const char* fa_status_string(fa_status s);
 

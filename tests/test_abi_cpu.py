@@ -145,3 +145,10 @@ def test_product_path_never_touches_the_oracle():
                 assert not re.search(r"^\s*(from|import)\s+oracle\b|oracle[/.]attention|"
                                      r"attn_(fwd|bwd|tiled|rows)_ref", text, re.M), \
                     os.path.join(dirpath, f)
+
+
+def test_profile_hook_argument_check():
+    lib = _lib()
+    assert lib.fa_profile_backward_main(P, None) == B.FA_ERR_INVALID_ARG
+    assert lib.fa_profile_backward_main(None, P) == B.FA_ERR_INVALID_ARG
+    assert lib.fa_profile_backward_main(None, None) == B.FA_OK
