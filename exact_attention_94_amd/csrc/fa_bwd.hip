@@ -154,37 +154,41 @@ __global__ __launch_bounds__(256, Bwd<D>::MIN_WG) void bwd_main_kernel(BwdArgs a
   }
   (void)n_kt;
   const size_t head_off = (size_t)bh * N * D;
-  const uint16_t* __restrict__ qh = static_cast<const uint16_t*>(a.q) + head_off;
-  const uint16_t* __restrict__ kh = static_cast<const uint16_t*>(a.k) + head_off;
-  const uint16_t* __restrict__ vh = static_cast<const uint16_t*>(a.v) + head_off;
-  const uint16_t* __restrict__ doh = static_cast<const uint16_t*>(a.dout) + head_off;
-  const float* __restrict__ lseh = a.lse + (size_t)bh * N;
-  const float* __restrict__ delh = a.delta + (size_t)bh * N;
-  float* __restrict__ dqh = a.dq_acc + head_off;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const auto qrs = make_rsrc(static_cast<const uint16_t*>(a.q) + head_off, head_bytes);
+  const auto krs = make_rsrc(static_cast<const uint16_t*>(a.k) + head_off, head_bytes);
+  const auto vrs = make_rsrc(static_cast<const uint16_t*>(a.v) + head_off, head_bytes);
+  const auto dors = make_rsrc(static_cast<const uint16_t*>(a.dout) + head_off, head_bytes);
+  const auto lrs = make_rsrc(a.lse + (size_t)bh * N, (uint32_t)N * 4);
+  const auto drs = make_rsrc(a.delta + (size_t)bh * N, (uint32_t)N * 4);
+  const auto dqrs = make_rsrc(a.dq_acc + head_off, (uint32_t)N * D * 4);
 
   const int k0 = kt * C::BKV;
   const int kw0 = k0 + wave * 32;  // this wave's first key
   const int key = kw0 + r;         // the key this lane owns in every accumulator
 
-  // K and V of this wave as B operands (fp16): key kw0 + r, d = 16*ks + 8*g .. +8.
+  // K and V of this wave as B operands (fp16): key kw0 + r, d = 16*ks + 8*g .. +8 (zeros
+  // beyond N).
   Frag16 kf[C::KS], vf[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
-    const bool in = key < N;
-    kf[ks].w = in ? to_f16x8<IS_BF16>(ld16(kh + (size_t)key * D + ks * 16 + g * 8)) : u32x4{0, 0, 0, 0};
-    vf[ks].w = in ? to_f16x8<IS_BF16>(ld16(vh + (size_t)key * D + ks * 16 + g * 8)) : u32x4{0, 0, 0, 0};
+    const uint32_t off = (uint32_t)(key * D + ks * 16 + g * 8) * 2;
+    kf[ks].w = to_f16x8<IS_BF16>(buf_ld16(krs, off));
+    vf[ks].w = to_f16x8<IS_BF16>(buf_ld16(vrs, off));
   }
   // K^T of the whole workgroup in LDS (B operand of dQ = dS K).
-  for (int u = tid; u < (C::BKV / 2) * (D / 8); u += C::NT) {
-    const int pair = u % (C::BKV / 2), cc = u / (C::BKV / 2);
-    const int gk = k0 + 2 * pair;
-    const u32x4 x0 = gk < N ? to_f16x8<IS_BF16>(ld16(kh + (size_t)gk * D + cc * 8)) : u32x4{0, 0, 0, 0};
-    const u32x4 x1 = gk + 1 < N ? to_f16x8<IS_BF16>(ld16(kh + (size_t)(gk + 1) * D + cc * 8)) : u32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int u = 0; u < (C::BKV / 2) * (D / 8) / C::NT; ++u) {
+    const int unit = tid + u * C::NT;
+    const int pair = unit % (C::BKV / 2), cc = unit / (C::BKV / 2);
+    const uint32_t off = (uint32_t)((k0 + 2 * pair) * D + cc * 8) * 2;
+    const u32x4 x0 = to_f16x8<IS_BF16>(buf_ld16(krs, off));
+    const u32x4 x1 = to_f16x8<IS_BF16>(buf_ld16(krs, off + D * 2));
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const int d0 = cc * 8 + 2 * w;
-      *reinterpret_cast<uint32_t*>(Kt + d0 * C::SROW + 2 * pair) = (x0[w] & 0xFFFFu) | (x1[w] << 16);
-      *reinterpret_cast<uint32_t*>(Kt + (d0 + 1) * C::SROW + 2 * pair) = (x0[w] >> 16) | (x1[w] & 0xFFFF0000u);
+      *reinterpret_cast<uint32_t*>(Kt + d0 * C::SROW + 2 * pair) = __builtin_amdgcn_perm(x1[w], x0[w], 0x05040100u);
+      *reinterpret_cast<uint32_t*>(Kt + (d0 + 1) * C::SROW + 2 * pair) = __builtin_amdgcn_perm(x1[w], x0[w], 0x07060302u);
     }
   }
 
@@ -199,9 +203,10 @@ __global__ __launch_bounds__(256, Bwd<D>::MIN_WG) void bwd_main_kernel(BwdArgs a
 
   const float c = a.c;
   const int q_begin = CAUSAL ? (k0 / C::BQ) * C::BQ : 0;
-  const int n_steps = (N - q_begin + C::BQ - 1) / C::BQ;
+  const int n_steps = (N - q_begin + C::BQ - 1) / C::BQ;  // >= 1: k0 < N
 
-  // Prefetch registers for one Q / dO tile.
+  // Prefetch registers for one Q / dO tile and its LSE / D values (rows beyond N read as 0;
+  // their LSE is set to +inf so that P = 0 there).
   u32x4 qreg[C::UNITS][2], oreg[C::UNITS][2];
   float lreg = 0.f, dreg = 0.f;
   auto load_tile = [&](int i0) {
@@ -209,19 +214,16 @@ __global__ __launch_bounds__(256, Bwd<D>::MIN_WG) void bwd_main_kernel(BwdArgs a
     for (int u = 0; u < C::UNITS; ++u) {
       const int unit = tid + u * C::NT;
       const int pair = unit % (C::BQ / 2), cc = unit / (C::BQ / 2);
-      const int gq = i0 + 2 * pair;
-      qreg[u][0] = gq < N ? ld16(qh + (size_t)gq * D + cc * 8) : u32x4{0, 0, 0, 0};
-      qreg[u][1] = gq + 1 < N ? ld16(qh + (size_t)(gq + 1) * D + cc * 8) : u32x4{0, 0, 0, 0};
-      oreg[u][0] = gq < N ? ld16(doh + (size_t)gq * D + cc * 8) : u32x4{0, 0, 0, 0};
-      oreg[u][1] = gq + 1 < N ? ld16(doh + (size_t)(gq + 1) * D + cc * 8) : u32x4{0, 0, 0, 0};
+      const uint32_t off = (uint32_t)((i0 + 2 * pair) * D + cc * 8) * 2;
+      qreg[u][0] = buf_ld16(qrs, off);
+      qreg[u][1] = buf_ld16(qrs, off + D * 2);
+      oreg[u][0] = buf_ld16(dors, off);
+      oreg[u][1] = buf_ld16(dors, off + D * 2);
     }
-    if (tid < C::BQ) {
-      const int gq = i0 + tid;
-      lreg = gq < N ? lseh[gq] * kLog2e : INFINITY;  // P = 0 for rows beyond N
-      dreg = gq < N ? delh[gq] : 0.f;
-    }
+    lreg = buf_ldf(lrs, (uint32_t)(i0 + lane) * 4);
+    dreg = buf_ldf(drs, (uint32_t)(i0 + lane) * 4);
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int i0) {
 #pragma unroll
     for (int u = 0; u < C::UNITS; ++u) {
       const int unit = tid + u * C::NT;
@@ -237,22 +239,21 @@ __global__ __launch_bounds__(256, Bwd<D>::MIN_WG) void bwd_main_kernel(BwdArgs a
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const int d0 = cc * 8 + 2 * w;
-        *reinterpret_cast<uint32_t*>(Qt + d0 * C::TROW + qa) = (q0[w] & 0xFFFFu) | (q1[w] << 16);
-        *reinterpret_cast<uint32_t*>(Qt + (d0 + 1) * C::TROW + qa) = (q0[w] >> 16) | (q1[w] & 0xFFFF0000u);
-        *reinterpret_cast<uint32_t*>(dOt + d0 * C::TROW + qa) = (o0[w] & 0xFFFFu) | (o1[w] << 16);
-        *reinterpret_cast<uint32_t*>(dOt + (d0 + 1) * C::TROW + qa) = (o0[w] >> 16) | (o1[w] & 0xFFFF0000u);
+        *reinterpret_cast<uint32_t*>(Qt + d0 * C::TROW + qa) = __builtin_amdgcn_perm(q1[w], q0[w], 0x05040100u);
+        *reinterpret_cast<uint32_t*>(Qt + (d0 + 1) * C::TROW + qa) = __builtin_amdgcn_perm(q1[w], q0[w], 0x07060302u);
+        *reinterpret_cast<uint32_t*>(dOt + d0 * C::TROW + qa) = __builtin_amdgcn_perm(o1[w], o0[w], 0x05040100u);
+        *reinterpret_cast<uint32_t*>(dOt + (d0 + 1) * C::TROW + qa) = __builtin_amdgcn_perm(o1[w], o0[w], 0x07060302u);
       }
     }
-    if (tid < C::BQ) {
-      lse_s[tid] = lreg;
-      del_s[tid] = dreg;
+    if (wave == 0) {
+      lse_s[lane] = (i0 + lane < N) ? lreg * kLog2e : INFINITY;
+      del_s[lane] = dreg;
     }
   };
 
-  if (n_steps > 0) {
-    load_tile(q_begin);
-    store_tile();
-  }
+  load_tile(q_begin);
+  store_tile(q_begin);
+  wait_vmem_all();
   __syncthreads();
 
   for (int step = 0; step < n_steps; ++step) {
@@ -339,7 +340,7 @@ __global__ __launch_bounds__(256, Bwd<D>::MIN_WG) void bwd_main_kernel(BwdArgs a
     __syncthreads();
 
     // ---- phase B: next tile into LDS; dQ(tile) += scale * dS K over the 128 keys ------------
-    if (step + 1 < n_steps) store_tile();
+    if (step + 1 < n_steps) store_tile(i0 + C::BQ);
 #pragma unroll
     for (int bi = 0; bi < C::DQ_BLOCKS; ++bi) {
       const int blk = wave * C::DQ_BLOCKS + bi;
@@ -358,7 +359,7 @@ __global__ __launch_bounds__(256, Bwd<D>::MIN_WG) void bwd_main_kernel(BwdArgs a
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int q = i0 + qb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-        if (q < N) unsafeAtomicAdd(dqh + (size_t)q * D + db * 32 + r, acc[i] * a.scale);
+        buf_atomic_add(dqrs, (uint32_t)(q * D + db * 32 + r) * 4, acc[i] * a.scale);
       }
     }
     __syncthreads();

@@ -41,17 +41,19 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const Frag16& a, const Frag16& b,
   }
 }
 
-// Round-to-nearest-even float -> 16-bit storage, two at a time (low half = a).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even float -> 16-bit storage, two at a time (low half = a); one
+// v_cvt_pk_{bf16,f16}_f32 instruction.
 template <bool IS_BF16>
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
+  const f32x2 v = {a, b};
   if constexpr (IS_BF16) {
-    __bf16 x = (__bf16)a, y = (__bf16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, x) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
   } else {
-    _Float16 x = (_Float16)a, y = (_Float16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, x) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
   }
 }
 
@@ -64,8 +66,52 @@ __device__ __forceinline__ float to_f32(uint16_t h) {
   }
 }
 
-// Value held by lane l ^ 32 (the other half of the wave).
+// Value held by lane l ^ 32 (the other half of the wave), through the LDS crossbar.
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
+
+// max / sum of x over lanes l and l ^ 32, with one v_permlane32_swap (VALU, no LDS). The swap
+// exchanges one half of the wave between its two operands; with both operands = x, the two
+// results hold x of lane l and of lane l ^ 32 in some order, so their max / sum is symmetric.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_min(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __builtin_fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Buffer resource over [base, base + bytes): 16-byte loads through it are branch-free and
+// return zeros when they fall outside the range (ragged tails need no predication, so the
+// compiler can count outstanding loads exactly and keep prefetches in flight).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+__device__ __forceinline__ float buf_ldf(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+// fp32 atomic add (no return) through a buffer resource; out-of-range adds are dropped.
+__device__ __forceinline__ void buf_atomic_add(__amdgpu_buffer_rsrc_t r, uint32_t byte_off,
+                                               float v) {
+  __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, byte_off, 0, 0);
+}
+
+// s_waitcnt vmcnt(0) (expcnt / lgkmcnt left at their maxima): every outstanding vector memory
+// load of this wave has completed. Used once before a main loop so that no wait on loads issued
+// before it (e.g. register-resident operands) ends up inside the loop, where it would also wait
+// for the loop's own prefetches.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
