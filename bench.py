@@ -166,7 +166,8 @@ def main():
     o = torch.empty(shape, dtype=torch.float32, device=dev)
     lse = torch.empty(shape[:3], dtype=torch.float32, device=dev)
     grads = tuple(torch.empty(shape, dtype=torch.float32, device=dev) for _ in range(3))
-    ws = torch.empty(fa.workspace_bytes(*shape, fa.FA_F32), dtype=torch.uint8, device=dev)
+    ws = torch.empty(fa.workspace_bytes(*shape, fa.FA_BF16, fa.FA_F32), dtype=torch.uint8,
+                     device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
 
     def step():

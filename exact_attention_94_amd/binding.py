@@ -44,7 +44,7 @@ def load(path=LIB_PATH):
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, vp]
     lib.fa_forward.restype = i
-    lib.fa_backward_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa_backward_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_backward_workspace_bytes.restype = sz
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, i,
                                 vp, sz, vp]
@@ -126,8 +126,8 @@ def profile_backward_main(before, after):
         raise FAError(st, "fa_profile_backward_main")
 
 
-def workspace_bytes(B, H, N, d, grad_dtype_code):
-    return int(load().fa_backward_workspace_bytes(B, H, N, d, grad_dtype_code))
+def workspace_bytes(B, H, N, d, in_dtype_code, grad_dtype_code):
+    return int(load().fa_backward_workspace_bytes(B, H, N, d, in_dtype_code, grad_dtype_code))
 
 
 def backward(q, k, v, o, dout, lse, scale=None, causal=False, grad_dtype=None, workspace=None,
@@ -148,7 +148,7 @@ def backward(q, k, v, o, dout, lse, scale=None, causal=False, grad_dtype=None, w
         grads = tuple(torch.empty((B, H, N, d), dtype=grad_dtype, device=q.device)
                       for _ in range(3))
     dq, dk, dv = grads
-    need = workspace_bytes(B, H, N, d, gcode)
+    need = workspace_bytes(B, H, N, d, dtype_code(q.dtype), gcode)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     st = load().fa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),

@@ -37,12 +37,20 @@ thread_local hipEvent_t t_prof_after = nullptr;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-size_t workspace_layout(int B, int H, int N, int d, fa_dtype grad_dtype, size_t* dq_off) {
+// Workspace: D (fp32 [B,H,N], 256-byte aligned) | fp32 dQ accumulator [B,H,N,d] when the
+// gradients are 16-bit | fp16 copies of Q, K, V, dO ([B,H,N,d] each) when the inputs are bf16.
+struct WsLayout {
+  size_t dq_off, f16_off, total;
+};
+
+WsLayout workspace_layout(int B, int H, int N, int d, fa_dtype in_dtype, fa_dtype grad_dtype) {
   const size_t rows = (size_t)B * H * N;
-  const size_t delta_bytes = round_up(rows * sizeof(float), 256);
-  *dq_off = delta_bytes;
-  const size_t dq_bytes = (grad_dtype == FA_F32) ? 0 : rows * (size_t)d * sizeof(float);
-  return delta_bytes + dq_bytes;
+  const size_t elems = rows * (size_t)d;
+  WsLayout w;
+  w.dq_off = round_up(rows * sizeof(float), 256);
+  w.f16_off = round_up(w.dq_off + ((grad_dtype == FA_F32) ? 0 : elems * sizeof(float)), 256);
+  w.total = w.f16_off + ((in_dtype == FA_BF16) ? 4 * elems * 2 : 0);
+  return w;
 }
 
 }  // namespace
@@ -87,10 +95,11 @@ fa_status fa_forward(const void* q, const void* k, const void* v, void* o, float
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-size_t fa_backward_workspace_bytes(int B, int H, int N, int d, fa_dtype grad_dtype) {
-  if (check_shape(B, H, N, d) != FA_OK || !valid_dtype(grad_dtype)) return 0;
-  size_t off = 0;
-  return workspace_layout(B, H, N, d, grad_dtype, &off);
+size_t fa_backward_workspace_bytes(int B, int H, int N, int d, fa_dtype in_dtype,
+                                   fa_dtype grad_dtype) {
+  if (check_shape(B, H, N, d) != FA_OK || !valid_dtype(in_dtype) || !valid_dtype(grad_dtype))
+    return 0;
+  return workspace_layout(B, H, N, d, in_dtype, grad_dtype).total;
 }
 
 fa_status fa_backward(const void* q, const void* k, const void* v, const void* o,
@@ -111,9 +120,9 @@ fa_status fa_backward(const void* q, const void* k, const void* v, const void* o
   if (in_dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   if (o_dtype != in_dtype && o_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
   if (grad_dtype != in_dtype && grad_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
-  size_t dq_off = 0;
-  const size_t need = workspace_layout(B, H, N, d, grad_dtype, &dq_off);
-  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const WsLayout ws = workspace_layout(B, H, N, d, in_dtype, grad_dtype);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < ws.total) return FA_ERR_WORKSPACE;
+  char* wsb = static_cast<char*>(workspace);
 
   fa::BwdArgs a{};
   a.q = q;
@@ -124,7 +133,20 @@ fa_status fa_backward(const void* q, const void* k, const void* v, const void* o
   a.lse = lse;
   a.delta = static_cast<float*>(workspace);
   a.dq_acc = (grad_dtype == FA_F32) ? static_cast<float*>(dq)
-                                     : reinterpret_cast<float*>(static_cast<char*>(workspace) + dq_off);
+                                     : reinterpret_cast<float*>(wsb + ws.dq_off);
+  if (in_dtype == FA_BF16) {
+    const size_t elems = (size_t)B * H * N * d;
+    uint16_t* f16 = reinterpret_cast<uint16_t*>(wsb + ws.f16_off);
+    a.q16 = f16;
+    a.k16 = f16 + elems;
+    a.v16 = f16 + 2 * elems;
+    a.do16 = f16 + 3 * elems;
+  } else {
+    a.q16 = static_cast<const uint16_t*>(q);
+    a.k16 = static_cast<const uint16_t*>(k);
+    a.v16 = static_cast<const uint16_t*>(v);
+    a.do16 = static_cast<const uint16_t*>(dout);
+  }
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;

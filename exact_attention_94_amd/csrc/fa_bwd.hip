@@ -9,25 +9,40 @@
 //
 // Kernels (one stream, in order):
 //   1. bwd_pre:   D = rowsum(dO * O) in fp32 from the forward's output; zero the fp32 dQ
-//                 accumulator.
+//                 accumulator; fp16 copies of bf16 Q, K, V, dO.
 //   2. bwd_main:  one workgroup per tile of 128 keys (4 waves x 32 keys). dK and dV stay in
 //                 registers for the whole loop over query tiles (causal: only tiles at or below
-//                 the diagonal). dS goes once through LDS (the only transpose on the path) and
+//                 the diagonal). dS goes once through LDS (stored as dS^T, read transposed) and
 //                 the workgroup's dQ contribution is added to the fp32 accumulator with atomics.
 //   3. dq_cast:   only for 16-bit gradients: fp32 accumulator -> output dtype.
 //
 // All five products run on v_mfma_f32_32x32x16_f16 with fp32 accumulation. bf16 inputs are
-// converted to fp16 when staged (exact while 2^-14 <= |x| <= 65504); P and dS are rounded to
-// fp16, whose 11-bit significand keeps the gradients of long peaked rows inside the error
-// budget that bf16 operands would exceed.
+// converted once to fp16 by bwd_pre into the workspace (exact while 2^-14 <= |x| <= 65504);
+// P and dS are rounded to fp16, whose 11-bit significand keeps the gradients of long peaked
+// rows inside the error budget that bf16 operands would exceed. Operands that the products
+// need transposed (Q^T, dO^T, dS, K for dQ) are read from row-major LDS tiles with
+// ds_read_b64_tr_b16, so every tile is staged once, in one layout.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
 namespace fa {
 
 // ----------------------------------------------------------------------------------------
-// 1. D = rowsum(dO * O); zero dq_acc.
+// 1. D = rowsum(dO * O); zero dq_acc; for bf16 inputs, fp16 copies of Q, K, V and dO.
 // ----------------------------------------------------------------------------------------
+template <bool IS_BF16>
+__device__ __forceinline__ u32x4 to_f16x8(u32x4 v) {
+  if constexpr (IS_BF16) {
+    u32x4 o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      o[w] = pack2<false>(__uint_as_float(v[w] << 16), __uint_as_float(v[w] & 0xFFFF0000u));
+    return o;
+  } else {
+    return v;
+  }
+}
+
 template <int D, bool IS_BF16, bool O_F32>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, long long rows) {
   constexpr int TPR = D / 8;  // threads per row, 8 elements each
@@ -62,6 +77,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, long long rows)
     float* dq = a.dq_acc + base;
     *reinterpret_cast<f32x4*>(dq) = f32x4{0.f, 0.f, 0.f, 0.f};
     *reinterpret_cast<f32x4*>(dq + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (IS_BF16) {
+      st16(const_cast<uint16_t*>(a.q16) + base, to_f16x8<true>(ld16(static_cast<const uint16_t*>(a.q) + base)));
+      st16(const_cast<uint16_t*>(a.k16) + base, to_f16x8<true>(ld16(static_cast<const uint16_t*>(a.k) + base)));
+      st16(const_cast<uint16_t*>(a.v16) + base, to_f16x8<true>(ld16(static_cast<const uint16_t*>(a.v) + base)));
+      st16(const_cast<uint16_t*>(a.do16) + base, to_f16x8<true>(dw));
+    }
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
@@ -78,23 +99,6 @@ __device__ __forceinline__ int qrow_of_query(int qq) {
   return 8 * (2 * (qq >> 4) + ((qq >> 2) & 1)) + 4 * ((qq >> 3) & 1) + (qq & 3);
 }
 
-template <bool IS_BF16>
-__device__ __forceinline__ uint32_t to_f16x2(uint32_t w) {
-  if constexpr (IS_BF16) {
-    const float lo = __uint_as_float(w << 16);
-    const float hi = __uint_as_float(w & 0xFFFF0000u);
-    return pack2<false>(lo, hi);
-  } else {
-    return w;
-  }
-}
-
-template <bool IS_BF16>
-__device__ __forceinline__ u32x4 to_f16x8(u32x4 v) {
-  return u32x4{to_f16x2<IS_BF16>(v[0]), to_f16x2<IS_BF16>(v[1]), to_f16x2<IS_BF16>(v[2]),
-               to_f16x2<IS_BF16>(v[3])};
-}
-
 template <int D>
 struct Bwd {
   static constexpr int NW = 4;
@@ -104,19 +108,16 @@ struct Bwd {
   static constexpr int QBS = BQ / 32;  // 32-query blocks per step
   static constexpr int KS = D / 16;    // contraction steps over d
   static constexpr int DB = D / 32;    // 32-row blocks over d
-  static constexpr int QROW = D + 8;   // Q / dO tile row stride (elements)
-  static constexpr int TROW = BQ + 8;  // Q^T / dO^T row stride
-  static constexpr int SROW = BKV + 8; // dS and K^T row stride
+  static constexpr int QROW = D + 8;   // Q / dO / K tile row stride (elements)
+  static constexpr int SROW = BQ + 8;  // dS^T row stride (elements)
   static constexpr int OFF_Q = 0;
   static constexpr int OFF_DO = OFF_Q + BQ * QROW;
-  static constexpr int OFF_QT = OFF_DO + BQ * QROW;
-  static constexpr int OFF_DOT = OFF_QT + D * TROW;
-  static constexpr int OFF_DS = OFF_DOT + D * TROW;
-  static constexpr int OFF_KT = OFF_DS + BQ * SROW;
-  static constexpr int OFF_VEC = OFF_KT + D * SROW;  // 16-bit element offset of the fp32 vectors
+  static constexpr int OFF_K = OFF_DO + BQ * QROW;
+  static constexpr int OFF_DS = OFF_K + BKV * QROW;
+  static constexpr int OFF_VEC = OFF_DS + BKV * SROW;  // 16-bit element offset of the fp32 vectors
   static constexpr int LDS_BYTES = OFF_VEC * 2 + 2 * BQ * 4;
-  static constexpr int UNITS = (BQ / 2) * (D / 8) / NT;  // (2 rows x 8 d) units per thread
-  static constexpr int DQ_BLOCKS = QBS * DB / NW;        // dQ 32x32 blocks per wave
+  static constexpr int CHUNKS = BQ * D / 8 / NT;  // 16-byte chunks per thread per tile
+  static constexpr int DQ_BLOCKS = QBS * DB / NW; // dQ 32x32 blocks per wave
   static constexpr int MIN_WG = (D == 64) ? 2 : 1;
 };
 
@@ -124,12 +125,10 @@ template <int D, bool IS_BF16, bool G_F32, bool CAUSAL>
 __global__ __launch_bounds__(256, Bwd<D>::MIN_WG) void bwd_main_kernel(BwdArgs a) {
   using C = Bwd<D>;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  uint16_t* Qs = smem + C::OFF_Q;
-  uint16_t* dOs = smem + C::OFF_DO;
-  uint16_t* Qt = smem + C::OFF_QT;
-  uint16_t* dOt = smem + C::OFF_DOT;
-  uint16_t* dSs = smem + C::OFF_DS;
-  uint16_t* Kt = smem + C::OFF_KT;
+  uint16_t* Qs = smem + C::OFF_Q;    // [BQ][QROW], rows in qrow_of_query order per 32 block
+  uint16_t* dOs = smem + C::OFF_DO;  // same layout as Qs
+  uint16_t* Ks = smem + C::OFF_K;    // [BKV][QROW], keys in order
+  uint16_t* dSt = smem + C::OFF_DS;  // dS^T: [BKV][SROW], queries in order
   float* lse_s = reinterpret_cast<float*>(smem + C::OFF_VEC);
   float* del_s = lse_s + C::BQ;
 
@@ -140,8 +139,8 @@ __global__ __launch_bounds__(256, Bwd<D>::MIN_WG) void bwd_main_kernel(BwdArgs a
   const int r = lane & 31;
   const int N = a.N;
 
-  // Workgroup -> (head, key tile); causal: the longest (first) key tiles are dispatched first.
-  const int n_kt = a.n_tiles;
+  // Workgroup -> (head, key tile); causal: the longest (first) key tiles are dispatched first;
+  // with B*H a multiple of 8 each XCD works on its own heads.
   int bh, kt;
   if ((a.bh & 7) == 0) {
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, hp = a.bh >> 3;
@@ -152,13 +151,12 @@ __global__ __launch_bounds__(256, Bwd<D>::MIN_WG) void bwd_main_kernel(BwdArgs a
     kt = blockIdx.x / a.bh;
     bh = blockIdx.x - kt * a.bh;
   }
-  (void)n_kt;
   const size_t head_off = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const auto qrs = make_rsrc(static_cast<const uint16_t*>(a.q) + head_off, head_bytes);
-  const auto krs = make_rsrc(static_cast<const uint16_t*>(a.k) + head_off, head_bytes);
-  const auto vrs = make_rsrc(static_cast<const uint16_t*>(a.v) + head_off, head_bytes);
-  const auto dors = make_rsrc(static_cast<const uint16_t*>(a.dout) + head_off, head_bytes);
+  const auto qrs = make_rsrc(a.q16 + head_off, head_bytes);
+  const auto krs = make_rsrc(a.k16 + head_off, head_bytes);
+  const auto vrs = make_rsrc(a.v16 + head_off, head_bytes);
+  const auto dors = make_rsrc(a.do16 + head_off, head_bytes);
   const auto lrs = make_rsrc(a.lse + (size_t)bh * N, (uint32_t)N * 4);
   const auto drs = make_rsrc(a.delta + (size_t)bh * N, (uint32_t)N * 4);
   const auto dqrs = make_rsrc(a.dq_acc + head_off, (uint32_t)N * D * 4);
@@ -167,29 +165,20 @@ __global__ __launch_bounds__(256, Bwd<D>::MIN_WG) void bwd_main_kernel(BwdArgs a
   const int kw0 = k0 + wave * 32;  // this wave's first key
   const int key = kw0 + r;         // the key this lane owns in every accumulator
 
-  // K and V of this wave as B operands (fp16): key kw0 + r, d = 16*ks + 8*g .. +8 (zeros
-  // beyond N).
+  // K and V of this wave as B operands: key kw0 + r, d = 16*ks + 8*g .. +8 (zeros beyond N).
   Frag16 kf[C::KS], vf[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
     const uint32_t off = (uint32_t)(key * D + ks * 16 + g * 8) * 2;
-    kf[ks].w = to_f16x8<IS_BF16>(buf_ld16(krs, off));
-    vf[ks].w = to_f16x8<IS_BF16>(buf_ld16(vrs, off));
+    kf[ks].w = buf_ld16(krs, off);
+    vf[ks].w = buf_ld16(vrs, off);
   }
-  // K^T of the whole workgroup in LDS (B operand of dQ = dS K).
+  // K of the whole workgroup in LDS (B operand of dQ = dS K, read transposed).
 #pragma unroll
-  for (int u = 0; u < (C::BKV / 2) * (D / 8) / C::NT; ++u) {
-    const int unit = tid + u * C::NT;
-    const int pair = unit % (C::BKV / 2), cc = unit / (C::BKV / 2);
-    const uint32_t off = (uint32_t)((k0 + 2 * pair) * D + cc * 8) * 2;
-    const u32x4 x0 = to_f16x8<IS_BF16>(buf_ld16(krs, off));
-    const u32x4 x1 = to_f16x8<IS_BF16>(buf_ld16(krs, off + D * 2));
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int d0 = cc * 8 + 2 * w;
-      *reinterpret_cast<uint32_t*>(Kt + d0 * C::SROW + 2 * pair) = __builtin_amdgcn_perm(x1[w], x0[w], 0x05040100u);
-      *reinterpret_cast<uint32_t*>(Kt + (d0 + 1) * C::SROW + 2 * pair) = __builtin_amdgcn_perm(x1[w], x0[w], 0x07060302u);
-    }
+  for (int i = 0; i < C::BKV * D / 8 / C::NT; ++i) {
+    const int chunk = tid + i * C::NT;
+    const int kk = chunk / (D / 8), cc = chunk % (D / 8);
+    st16(Ks + kk * C::QROW + cc * 8, buf_ld16(krs, (uint32_t)(k0 * D + chunk * 8) * 2));
   }
 
   f32x16 dvacc[C::DB], dkacc[C::DB];
@@ -206,44 +195,27 @@ __global__ __launch_bounds__(256, Bwd<D>::MIN_WG) void bwd_main_kernel(BwdArgs a
   const int n_steps = (N - q_begin + C::BQ - 1) / C::BQ;  // >= 1: k0 < N
 
   // Prefetch registers for one Q / dO tile and its LSE / D values (rows beyond N read as 0;
-  // their LSE is set to +inf so that P = 0 there).
-  u32x4 qreg[C::UNITS][2], oreg[C::UNITS][2];
+  // their LSE is set to +inf when staged so that P = 0 there).
+  u32x4 qreg[C::CHUNKS], oreg[C::CHUNKS];
   float lreg = 0.f, dreg = 0.f;
   auto load_tile = [&](int i0) {
 #pragma unroll
-    for (int u = 0; u < C::UNITS; ++u) {
-      const int unit = tid + u * C::NT;
-      const int pair = unit % (C::BQ / 2), cc = unit / (C::BQ / 2);
-      const uint32_t off = (uint32_t)((i0 + 2 * pair) * D + cc * 8) * 2;
-      qreg[u][0] = buf_ld16(qrs, off);
-      qreg[u][1] = buf_ld16(qrs, off + D * 2);
-      oreg[u][0] = buf_ld16(dors, off);
-      oreg[u][1] = buf_ld16(dors, off + D * 2);
+    for (int u = 0; u < C::CHUNKS; ++u) {
+      const uint32_t off = (uint32_t)(i0 * D + (tid + u * C::NT) * 8) * 2;
+      qreg[u] = buf_ld16(qrs, off);
+      oreg[u] = buf_ld16(dors, off);
     }
     lreg = buf_ldf(lrs, (uint32_t)(i0 + lane) * 4);
     dreg = buf_ldf(drs, (uint32_t)(i0 + lane) * 4);
   };
   auto store_tile = [&](int i0) {
 #pragma unroll
-    for (int u = 0; u < C::UNITS; ++u) {
-      const int unit = tid + u * C::NT;
-      const int pair = unit % (C::BQ / 2), cc = unit / (C::BQ / 2);
-      const u32x4 q0 = to_f16x8<IS_BF16>(qreg[u][0]), q1 = to_f16x8<IS_BF16>(qreg[u][1]);
-      const u32x4 o0 = to_f16x8<IS_BF16>(oreg[u][0]), o1 = to_f16x8<IS_BF16>(oreg[u][1]);
-      const int qa = 2 * pair, qb_ = 2 * pair + 1;
-      const int ra = (qa & ~31) + qrow_of_query(qa & 31), rb = (qb_ & ~31) + qrow_of_query(qb_ & 31);
-      st16(Qs + ra * C::QROW + cc * 8, q0);
-      st16(Qs + rb * C::QROW + cc * 8, q1);
-      st16(dOs + ra * C::QROW + cc * 8, o0);
-      st16(dOs + rb * C::QROW + cc * 8, o1);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int d0 = cc * 8 + 2 * w;
-        *reinterpret_cast<uint32_t*>(Qt + d0 * C::TROW + qa) = __builtin_amdgcn_perm(q1[w], q0[w], 0x05040100u);
-        *reinterpret_cast<uint32_t*>(Qt + (d0 + 1) * C::TROW + qa) = __builtin_amdgcn_perm(q1[w], q0[w], 0x07060302u);
-        *reinterpret_cast<uint32_t*>(dOt + d0 * C::TROW + qa) = __builtin_amdgcn_perm(o1[w], o0[w], 0x05040100u);
-        *reinterpret_cast<uint32_t*>(dOt + (d0 + 1) * C::TROW + qa) = __builtin_amdgcn_perm(o1[w], o0[w], 0x07060302u);
-      }
+    for (int u = 0; u < C::CHUNKS; ++u) {
+      const int chunk = tid + u * C::NT;
+      const int qq = chunk / (D / 8), cc = chunk % (D / 8);
+      const int row = (qq & ~31) + qrow_of_query(qq & 31);
+      st16(Qs + row * C::QROW + cc * 8, qreg[u]);
+      st16(dOs + row * C::QROW + cc * 8, oreg[u]);
     }
     if (wave == 0) {
       lse_s[lane] = (i0 + lane < N) ? lreg * kLog2e : INFINITY;
@@ -271,6 +243,7 @@ __global__ __launch_bounds__(256, Bwd<D>::MIN_WG) void bwd_main_kernel(BwdArgs a
           sacc[qb][i] = 0.f;
           pacc[qb][i] = 0.f;
         }
+      // S = Q K^T and dP = dO V^T (rows: queries, columns: this wave's keys).
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
@@ -282,7 +255,9 @@ __global__ __launch_bounds__(256, Bwd<D>::MIN_WG) void bwd_main_kernel(BwdArgs a
           pacc[qb] = mfma32x32x16<false>(da, vf[ks], pacc[qb]);
         }
       }
-      // P = exp2(c*S - LSE*log2e); dS = P * (dP - D). Slot i: query i0 + 32*qb + 16*(i/8) + 8*g + i%8.
+      // P = exp2(c*S - LSE*log2e); dS = P * (dP - D).
+      // Slot i: query i0 + 32*qb + 16*(i/8) + 8*g + i%8.
+      const bool need_mask = (k0 + C::BKV > N) || (CAUSAL && (i0 < kw0 + 31));
       Frag16 pfr[C::QBS][2], dsf[C::QBS][2];
 #pragma unroll
       for (int qb = 0; qb < C::QBS; ++qb) {
@@ -298,10 +273,12 @@ __global__ __launch_bounds__(256, Bwd<D>::MIN_WG) void bwd_main_kernel(BwdArgs a
           for (int e = 0; e < 8; ++e) {
             const float lv = e < 4 ? l0[e] : l1[e - 4];
             const float dv = e < 4 ? d0[e] : d1[e - 4];
-            const int q = i0 + qloc + e;
             float pv = fast_exp2(__builtin_fmaf(sacc[qb][h * 8 + e], c, -lv));
-            const bool dead = (key >= N) || (CAUSAL && key > q);
-            pv = dead ? 0.f : pv;
+            if (need_mask) {
+              const int q = i0 + qloc + e;
+              const bool dead = (key >= N) || (CAUSAL && key > q);
+              pv = dead ? 0.f : pv;
+            }
             p[e] = pv;
             ds[e] = pv * (pacc[qb][h * 8 + e] - dv);
           }
@@ -309,24 +286,23 @@ __global__ __launch_bounds__(256, Bwd<D>::MIN_WG) void bwd_main_kernel(BwdArgs a
                                pack2<false>(p[4], p[5]), pack2<false>(p[6], p[7])};
           dsf[qb][h].w = u32x4{pack2<false>(ds[0], ds[1]), pack2<false>(ds[2], ds[3]),
                                pack2<false>(ds[4], ds[5]), pack2<false>(ds[6], ds[7])};
-          // dS -> LDS as dS[q][key] for the dQ product.
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            dSs[(qloc + 2 * w) * C::SROW + wave * 32 + r] = (uint16_t)(dsf[qb][h].w[w] & 0xFFFFu);
-            dSs[(qloc + 2 * w + 1) * C::SROW + wave * 32 + r] = (uint16_t)(dsf[qb][h].w[w] >> 16);
-          }
+          // dS^T[key][queries qloc .. qloc + 7] for the dQ product.
+          st16(dSt + (wave * 32 + r) * C::SROW + qloc, dsf[qb][h].w);
         }
       }
-      // dV^T += dO^T P ; dK^T += Q^T dS   (rows d, columns = this wave's keys)
+      // dV^T += dO^T P ; dK^T += Q^T dS   (rows d, columns = this wave's keys). The A operands
+      // are Q / dO read transposed: slots 0..3 = LDS rows 32qb + 16h + 4g + s, slots 4..7 the
+      // same + 8 (queries 16h + 8g + s under the row permutation).
 #pragma unroll
       for (int qb = 0; qb < C::QBS; ++qb) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
+          const int row = qb * 32 + h * 16 + g * 4;
 #pragma unroll
           for (int db = 0; db < C::DB; ++db) {
             Frag16 ot, qt;
-            ot.w = *reinterpret_cast<const u32x4*>(dOt + (db * 32 + r) * C::TROW + qb * 32 + h * 16 + g * 8);
-            qt.w = *reinterpret_cast<const u32x4*>(Qt + (db * 32 + r) * C::TROW + qb * 32 + h * 16 + g * 8);
+            ot.w = lds_tr_frag(dOs, C::QROW, row, row + 8, db * 32);
+            qt.w = lds_tr_frag(Qs, C::QROW, row, row + 8, db * 32);
             dvacc[db] = mfma32x32x16<false>(ot, pfr[qb][h], dvacc[db]);
             dkacc[db] = mfma32x32x16<false>(qt, dsf[qb][h], dkacc[db]);
           }
@@ -335,7 +311,7 @@ __global__ __launch_bounds__(256, Bwd<D>::MIN_WG) void bwd_main_kernel(BwdArgs a
     } else {
       // Keys entirely after every query of this tile: dS is 0 for them.
 #pragma unroll
-      for (int qq = 0; qq < C::BQ; ++qq) dSs[qq * C::SROW + wave * 32 + r] = 0;
+      for (int qq = 0; qq < C::BQ; qq += 8) st16(dSt + (wave * 32 + r) * C::SROW + qq, u32x4{0, 0, 0, 0});
     }
     __syncthreads();
 
@@ -350,9 +326,10 @@ __global__ __launch_bounds__(256, Bwd<D>::MIN_WG) void bwd_main_kernel(BwdArgs a
       for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
       for (int t = 0; t < C::BKV / 16; ++t) {
+        // A = dS[q = 32qb + r][keys 16t + 8g + s], B = K[keys 16t + 8g + s][d = 32db + r].
         Frag16 sa, kb;
-        sa.w = *reinterpret_cast<const u32x4*>(dSs + (qb * 32 + r) * C::SROW + t * 16 + g * 8);
-        kb.w = *reinterpret_cast<const u32x4*>(Kt + (db * 32 + r) * C::SROW + t * 16 + g * 8);
+        sa.w = lds_tr_frag(dSt, C::SROW, t * 16 + g * 8, t * 16 + g * 8 + 4, qb * 32);
+        kb.w = lds_tr_frag(Ks, C::QROW, t * 16 + g * 8, t * 16 + g * 8 + 4, db * 32);
         acc = mfma32x32x16<false>(sa, kb, acc);
       }
       // acc: column d = 32*db + r, rows = queries 8*(i/4) + 4*g + i%4 of block qb.

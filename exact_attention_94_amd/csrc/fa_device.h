@@ -88,6 +88,29 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// MFMA operand (8 x 16-bit, A or B) for lane l = 32*g + n, built from a row-major LDS tile X
+// (`stride` elements per row) with two ds_read_b64_tr_b16:
+//   slots 0..3 = X[row_lo + s][col0 + n],   slots 4..7 = X[row_hi + s - 4][col0 + n],
+// where row_lo / row_hi already include this lane's g. ds_read_b64_tr_b16 works on groups of 16
+// lanes: output lane i of a group receives, in slot k, element i % 4 of the 8 bytes addressed
+// by lane 4k + i/4 of that group. Lane 4k + j therefore addresses row base + k, columns
+// col0 + 16*(n / 16) + 4j .. +3, and output lane i gets column col0 + 16*(n / 16) + i = col0 + n.
+__device__ __forceinline__ u32x4 lds_tr_frag(const uint16_t* tile, int stride, int row_lo,
+                                             int row_hi, int col0) {
+  const int lane = threadIdx.x & 63;
+  const int col = col0 + (lane & 16) + 4 * (lane & 3);
+  const int dr = (lane >> 2) & 3;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(tile + (row_lo + dr) * stride + col));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(tile + (row_hi + dr) * stride + col));
+  const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
 // Buffer resource over [base, base + bytes): 16-byte loads through it are branch-free and
 // return zeros when they fall outside the range (ragged tails need no predication, so the
 // compiler can count outstanding loads exactly and keep prefetches in flight).

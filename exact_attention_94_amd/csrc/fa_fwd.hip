@@ -17,7 +17,8 @@
 //     in-lane plus one exchange between the two wave halves, and m, l, corr are lane-local;
 //   * K rows are placed in LDS in a permuted order so that a lane's 16 accumulator slots are
 //     keys {16*(i/8) + 8*g + i%8}: the probabilities then feed the P·V MFMA directly as its
-//     B operand (no LDS round trip), with V^T read as 16 contiguous bytes per lane;
+//     B operand (no LDS round trip); V stays in key order in LDS and its transposed operand is
+//     read with ds_read_b64_tr_b16;
 //   * exp2 with scale*log2(e) folded into one FMA per score;
 //   * K and V^T tiles are double-buffered in LDS (one barrier per K/V tile), the next tile's
 //     global loads are issued before the current tile's math;
@@ -63,14 +64,11 @@ struct Fwd16 {
   static constexpr int BC = 64;           // keys per K/V tile
   static constexpr int KS = D / 16;       // contraction steps of S^T = K Q^T
   static constexpr int DB = D / 32;       // 32-row blocks of O^T
-  static constexpr int KROW = D + 8;      // K tile row stride in LDS (elements)
-  static constexpr int VROW = BC + 8;     // V^T tile row stride in LDS (elements)
+  static constexpr int KROW = D + 8;      // K and V tile row stride in LDS (elements)
   static constexpr int KTILE = BC * KROW;
-  static constexpr int VTILE = D * VROW;
-  static constexpr int STAGE = KTILE + VTILE;  // elements per LDS stage
+  static constexpr int STAGE = 2 * KTILE;  // K then V, elements per LDS stage
   static constexpr int LDS_BYTES = 2 * STAGE * 2;
-  static constexpr int KCHUNKS = BC * D / 8 / NT;      // 16-byte K chunks per thread
-  static constexpr int VUNITS = (BC / 2) * (D / 8) / NT;  // (2 keys x 8 d) V units per thread
+  static constexpr int KCHUNKS = BC * D / 8 / NT;  // 16-byte chunks per thread per tensor
 };
 
 // Queries per wave (32 per MFMA column block). Two blocks halve the LDS reads per MFMA but, at
@@ -134,25 +132,17 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
   const int kv_end = CAUSAL ? min(N, qt0 + C::BR) : N;
   const int n_kt = (kv_end + C::BC - 1) / C::BC;
 
-  // Global -> register staging of one K/V tile (keys beyond N read as zeros).
-  u32x4 kreg[C::KCHUNKS];
-  u32x4 vreg[C::VUNITS][2];
+  // Global -> register staging of one K/V tile (keys beyond N read as zeros). K rows go to LDS
+  // in the permuted order of krow_of_key; V rows stay in key order (the P.V operand is read
+  // transposed by ds_read_b64_tr_b16).
+  u32x4 kreg[C::KCHUNKS], vreg[C::KCHUNKS];
   auto load_tile = [&](int j0) {
 #pragma unroll
     for (int i = 0; i < C::KCHUNKS; ++i) {
       const int chunk = tid + i * C::NT;
-      const int key = chunk / (D / 8);
-      const int cc = chunk % (D / 8);
-      kreg[i] = buf_ld16(krs, (uint32_t)((j0 + key) * D + cc * 8) * 2);
-    }
-#pragma unroll
-    for (int i = 0; i < C::VUNITS; ++i) {
-      const int unit = tid + i * C::NT;
-      const int pair = unit % (C::BC / 2);
-      const int cc = unit / (C::BC / 2);
-      const uint32_t off = (uint32_t)((j0 + 2 * pair) * D + cc * 8) * 2;
-      vreg[i][0] = buf_ld16(vrs, off);
-      vreg[i][1] = buf_ld16(vrs, off + D * 2);
+      const uint32_t off = (uint32_t)(j0 * D + chunk * 8) * 2;
+      kreg[i] = buf_ld16(krs, off);
+      vreg[i] = buf_ld16(vrs, off);
     }
   };
   auto store_tile = [&](int stage) {
@@ -165,22 +155,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
       const int cc = chunk % (D / 8);
       const int row = (key & ~31) + krow_of_key(key & 31);
       st16(ks_ + row * C::KROW + cc * 8, kreg[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < C::VUNITS; ++i) {
-      const int unit = tid + i * C::NT;
-      const int pair = unit % (C::BC / 2);
-      const int cc = unit / (C::BC / 2);
-      // (V[2p][d], V[2p+1][d]) -> one 32-bit word of V^T row d.
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t x0 = vreg[i][0][w], x1 = vreg[i][1][w];
-        const uint32_t lo = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
-        const uint32_t hi = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
-        const int d0 = cc * 8 + 2 * w;
-        *reinterpret_cast<uint32_t*>(vs_ + d0 * C::VROW + 2 * pair) = lo;
-        *reinterpret_cast<uint32_t*>(vs_ + (d0 + 1) * C::VROW + 2 * pair) = hi;
-      }
+      st16(vs_ + key * C::KROW + cc * 8, vreg[i]);
     }
   };
 
@@ -292,9 +267,10 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
           for (int db = 0; db < C::DB; ++db) {
+            // A operand V^T: lane (g, r) needs V[kb*32 + 16h + 8g + s][32*db + r], s = 0..7.
             Frag16 vf;
-            vf.w = *reinterpret_cast<const u32x4*>(vs_ + (db * 32 + r) * C::VROW + kb * 32 +
-                                                   h * 16 + g * 8);
+            const int row = kb * 32 + h * 16 + g * 8;
+            vf.w = lds_tr_frag(vs_, C::KROW, row, row + 4, db * 32);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
               oacc[db][qb] = mfma32x32x16<IS_BF16>(vf, pf[kb][h][qb], oacc[db][qb]);

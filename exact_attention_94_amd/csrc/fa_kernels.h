@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace fa {
 
@@ -30,6 +31,12 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* delta;   // float32 [B,H,N]: rowsum(dO * O)
+  // fp16 operands of the main kernel: the inputs themselves for fp16, copies made by the
+  // preprocess kernel (in the workspace) for bf16.
+  const uint16_t* q16;
+  const uint16_t* k16;
+  const uint16_t* v16;
+  const uint16_t* do16;
   int N;
   int bh;
   int n_tiles;

@@ -69,11 +69,13 @@ fa_status fa_forward(const void* q, const void* k, const void* v, void* o, float
                      fa_dtype o_dtype, void* stream);
 
 /*
- * Bytes of device workspace fa_backward needs for these sizes and grad_dtype: the row vector
- * D = rowsum(dO * O) (float32 [B,H,N]) plus, when grad_dtype is not FA_F32, a float32 [B,H,N,d]
- * accumulator for dQ. Returns 0 for arguments fa_backward would reject.
+ * Bytes of device workspace fa_backward needs for these sizes and dtypes: the row vector
+ * D = rowsum(dO * O) (float32 [B,H,N]); when grad_dtype is not FA_F32, a float32 [B,H,N,d]
+ * accumulator for dQ; when in_dtype is FA_BF16, fp16 copies of Q, K, V and dO (4 x [B,H,N,d]
+ * 16-bit) used as the MFMA operands. Returns 0 for arguments fa_backward would reject.
  */
-size_t fa_backward_workspace_bytes(int B, int H, int N, int d, fa_dtype grad_dtype);
+size_t fa_backward_workspace_bytes(int B, int H, int N, int d, fa_dtype in_dtype,
+                                   fa_dtype grad_dtype);
 
 /*
  * Backward pass ("FlashAttention 为什么不需要存下注意力矩阵" §03 3.3; "FlashAttention V1 技术深度解析"
@@ -84,7 +86,8 @@ size_t fa_backward_workspace_bytes(int B, int H, int N, int d, fa_dtype grad_dty
  *   dout       [B,H,N,d] in in_dtype, the upstream gradient dL/dO
  *   lse        [B,H,N] float32, the forward's logsumexp
  *   dq, dk, dv [B,H,N,d] in grad_dtype (in_dtype or FA_F32), written
- *   workspace  device buffer of at least fa_backward_workspace_bytes(B,H,N,d,grad_dtype) bytes,
+ *   workspace  device buffer of at least fa_backward_workspace_bytes(B,H,N,d,in_dtype,grad_dtype)
+ *              bytes,
  *              16-byte aligned; contents on entry are ignored and clobbered
  * The three gradient products and the dP product use fp16 MFMA operands with fp32
  * accumulation (bf16 inputs are converted exactly while |x| >= 2^-14). dQ is accumulated
