@@ -135,17 +135,19 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
   // Global -> register staging of one K/V tile (keys beyond N read as zeros). K rows go to LDS
   // in the permuted order of krow_of_key; V rows stay in key order (the P.V operand is read
   // transposed by ds_read_b64_tr_b16).
-  u32x4 kreg[C::KCHUNKS], vreg[C::KCHUNKS];
-  auto load_tile = [&](int j0) {
+  // Two register sets, so that the loads for tile j+2 are in flight while tile j+1 (loaded one
+  // iteration earlier) is written to LDS: each load has two iterations to arrive.
+  u32x4 kreg[2][C::KCHUNKS], vreg[2][C::KCHUNKS];
+  auto load_tile = [&](int set, int j0) {
 #pragma unroll
     for (int i = 0; i < C::KCHUNKS; ++i) {
       const int chunk = tid + i * C::NT;
       const uint32_t off = (uint32_t)(j0 * D + chunk * 8) * 2;
-      kreg[i] = buf_ld16(krs, off);
-      vreg[i] = buf_ld16(vrs, off);
+      kreg[set][i] = buf_ld16(krs, off);
+      vreg[set][i] = buf_ld16(vrs, off);
     }
   };
-  auto store_tile = [&](int stage) {
+  auto store_tile = [&](int set, int stage) {
     uint16_t* ks_ = smem + stage * C::STAGE;
     uint16_t* vs_ = ks_ + C::KTILE;
 #pragma unroll
@@ -154,132 +156,144 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
       const int key = chunk / (D / 8);
       const int cc = chunk % (D / 8);
       const int row = (key & ~31) + krow_of_key(key & 31);
-      st16(ks_ + row * C::KROW + cc * 8, kreg[i]);
-      st16(vs_ + key * C::KROW + cc * 8, vreg[i]);
+      st16(ks_ + row * C::KROW + cc * 8, kreg[set][i]);
+      st16(vs_ + key * C::KROW + cc * 8, vreg[set][i]);
     }
   };
 
-  // n_kt >= 1 always (N >= 1). Staging the first tile unconditionally also retires the Q loads
-  // before the loop, so no wait on them is left inside it.
-  load_tile(0);
-  store_tile(0);
-  wait_vmem_all();
-  __syncthreads();
+  // Math of one K/V tile already in LDS stage `stage`.
+  auto tile_math = [&](int stage, int j0) {
+      const bool wave_live = (j0 < kv_end) && (!CAUSAL || (j0 <= qw0 + QB * 32 - 1));
+      if (wave_live) {
+        const uint16_t* ks_ = smem + stage * C::STAGE;
+        const uint16_t* vs_ = ks_ + C::KTILE;
 
-  for (int jt = 0; jt < n_kt; ++jt) {
-    const int j0 = jt * C::BC;
-    const int stage = jt & 1;
-    if (jt + 1 < n_kt) load_tile(j0 + C::BC);
-
-    const bool wave_live = !CAUSAL || (j0 <= qw0 + QB * 32 - 1);
-    if (wave_live) {
-      const uint16_t* ks_ = smem + stage * C::STAGE;
-      const uint16_t* vs_ = ks_ + C::KTILE;
-
-      // ---- S^T = K Q^T ---------------------------------------------------------------
-      f32x16 sacc[2][QB];
+        // ---- S^T = K Q^T ---------------------------------------------------------------
+        f32x16 sacc[2][QB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sacc[kb][qb][i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          Frag16 kf;
-          kf.w = *reinterpret_cast<const u32x4*>(ks_ + (kb * 32 + r) * C::KROW + ks * 16 + g * 8);
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
-            sacc[kb][qb] = mfma32x32x16<IS_BF16>(kf, qf[qb][ks], sacc[kb][qb]);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sacc[kb][qb][i] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            Frag16 kf;
+            kf.w = *reinterpret_cast<const u32x4*>(ks_ + (kb * 32 + r) * C::KROW + ks * 16 + g * 8);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+              sacc[kb][qb] = mfma32x32x16<IS_BF16>(kf, qf[qb][ks], sacc[kb][qb]);
+          }
         }
-      }
 
-      // ---- mask: keys beyond N, and keys after the query on causal diagonal tiles ----------
-      const bool need_mask = (j0 + C::BC > N) || (CAUSAL && (j0 + C::BC - 1 > qw0));
-      if (need_mask) {
+        // ---- mask: keys beyond N, and keys after the query on causal diagonal tiles ----------
+        const bool need_mask = (j0 + C::BC > N) || (CAUSAL && (j0 + C::BC - 1 > qw0));
+        if (need_mask) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const int qrow = qw0 + qb * 32 + r;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int key = j0 + kb * 32 + (i >> 3) * 16 + g * 8 + (i & 7);
+                const bool dead = (key >= N) || (CAUSAL && key > qrow);
+                sacc[kb][qb][i] = dead ? masked : sacc[kb][qb][i];
+              }
+          }
+        }
+
+        // ---- online softmax (log2 domain): m, l, corr per query (lane-local) ----------------
+        Frag16 pf[2][2][QB];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          const int qrow = qw0 + qb * 32 + r;
+          float red = sacc[0][qb][0];
+          if (c_pos) {
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = j0 + kb * 32 + (i >> 3) * 16 + g * 8 + (i & 7);
-              const bool dead = (key >= N) || (CAUSAL && key > qrow);
-              sacc[kb][qb][i] = dead ? masked : sacc[kb][qb][i];
+              for (int i = 0; i < 16; ++i) red = __builtin_fmaxf(red, sacc[kb][qb][i]);
+            red = halves_max(red);
+          } else {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) red = __builtin_fminf(red, sacc[kb][qb][i]);
+            red = halves_min(red);
+          }
+          const float m_blk = red * c;  // -inf when the whole tile is masked for this query
+          const float m_new = __builtin_fmaxf(m_run[qb], m_blk);
+          const float corr = fast_exp2(m_run[qb] - m_new);
+          m_run[qb] = m_new;
+          float lsum = 0.f;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              float p[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                p[e] = fast_exp2(__builtin_fmaf(sacc[kb][qb][h * 8 + e], c, -m_new));
+                lsum += p[e];
+              }
+              pf[kb][h][qb].w = u32x4{pack2<IS_BF16>(p[0], p[1]), pack2<IS_BF16>(p[2], p[3]),
+                                      pack2<IS_BF16>(p[4], p[5]), pack2<IS_BF16>(p[6], p[7])};
             }
+          }
+          l_run[qb] = l_run[qb] * corr + lsum;
+          // Rescale the accumulator only when some lane's maximum moved (corr == 1 is identity).
+          if (__builtin_amdgcn_ballot_w64(corr != 1.f)) {
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) oacc[db][qb][i] *= corr;
+          }
         }
-      }
 
-      // ---- online softmax (log2 domain): m, l, corr per query (lane-local) ----------------
-      Frag16 pf[2][2][QB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float red = sacc[0][qb][0];
-        if (c_pos) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) red = __builtin_fmaxf(red, sacc[kb][qb][i]);
-          red = halves_max(red);
-        } else {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) red = __builtin_fminf(red, sacc[kb][qb][i]);
-          red = halves_min(red);
-        }
-        const float m_blk = red * c;  // -inf when the whole tile is masked for this query
-        const float m_new = __builtin_fmaxf(m_run[qb], m_blk);
-        const float corr = fast_exp2(m_run[qb] - m_new);
-        m_run[qb] = m_new;
-        float lsum = 0.f;
+        // ---- O^T += V^T P^T -----------------------------------------------------------------
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            float p[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              p[e] = fast_exp2(__builtin_fmaf(sacc[kb][qb][h * 8 + e], c, -m_new));
-              lsum += p[e];
+            for (int db = 0; db < C::DB; ++db) {
+              // A operand V^T: lane (g, r) needs V[kb*32 + 16h + 8g + s][32*db + r], s = 0..7.
+              Frag16 vf;
+              const int row = kb * 32 + h * 16 + g * 8;
+              vf.w = lds_tr_frag(vs_, C::KROW, row, row + 4, db * 32);
+#pragma unroll
+              for (int qb = 0; qb < QB; ++qb)
+                oacc[db][qb] = mfma32x32x16<IS_BF16>(vf, pf[kb][h][qb], oacc[db][qb]);
             }
-            pf[kb][h][qb].w = u32x4{pack2<IS_BF16>(p[0], p[1]), pack2<IS_BF16>(p[2], p[3]),
-                                    pack2<IS_BF16>(p[4], p[5]), pack2<IS_BF16>(p[6], p[7])};
-          }
-        }
-        l_run[qb] = l_run[qb] * corr + lsum;
-        // Rescale the accumulator only when some lane's maximum moved (corr == 1 is identity).
-        if (__builtin_amdgcn_ballot_w64(corr != 1.f)) {
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[db][qb][i] *= corr;
-        }
-      }
-
-      // ---- O^T += V^T P^T -----------------------------------------------------------------
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db) {
-            // A operand V^T: lane (g, r) needs V[kb*32 + 16h + 8g + s][32*db + r], s = 0..7.
-            Frag16 vf;
-            const int row = kb * 32 + h * 16 + g * 8;
-            vf.w = lds_tr_frag(vs_, C::KROW, row, row + 4, db * 32);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-              oacc[db][qb] = mfma32x32x16<IS_BF16>(vf, pf[kb][h][qb], oacc[db][qb]);
           }
         }
       }
-    }
 
-    if (jt + 1 < n_kt) store_tile(stage ^ 1);
+  };
+
+  // n_kt >= 1 always (N >= 1). The prologue stages tile 0; the explicit wait retires the Q loads
+  // before the loop; tile 1 is then in flight when the loop starts. Every load and LDS write in
+  // the loop is unconditional (tiles past the end read zeros and their math is skipped), so the
+  // compiler counts outstanding loads exactly.
+  load_tile(0, 0);
+  store_tile(0, 0);
+  wait_vmem_all();
+  load_tile(1, C::BC);
+  __syncthreads();
+
+  // Iteration jt: start loading tile jt+2, do the math of tile jt, write tile jt+1 (loaded during
+  // the previous iteration) into the other LDS stage, barrier. Unrolled by two so that register
+  // sets and LDS stages are compile-time.
+  for (int jt = 0; jt < n_kt; jt += 2) {
+    load_tile(0, (jt + 2) * C::BC);
+    tile_math(0, jt * C::BC);
+    store_tile(1, 1);
+    __syncthreads();
+    load_tile(1, (jt + 3) * C::BC);
+    tile_math(1, (jt + 1) * C::BC);
+    store_tile(0, 0);
     __syncthreads();
   }
 
