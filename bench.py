@@ -4,11 +4,14 @@
 One step = fa_forward + fa_backward over the headline workload (B=2, H=16, N=4096, d=64, causal,
 bf16 inputs; O and the gradients in fp32), inputs resident in HBM before timing starts.
 Prints ONE JSON line with the step throughput, the forward and backward TFLOP/s and their share of
-the MI355X dense bf16/fp16 MFMA peak, a roofline record for the dominant kernel (the main backward
-kernel, timed alone with HIP events that the library records around its launch), and the float64
-CPU oracle timed on a bounded sample of the same workload on this host.
+the MI355X dense bf16/fp16 MFMA peak, a roofline record for the dominant kernel (the backward's
+dK/dV kernel, timed alone with HIP events that the library records around its launch), and the
+float64 CPU oracle timed on a bounded sample of the same workload on this host.
 
-FLOP convention: forward 4*B*H*N^2*d, halved when causal; backward 2.5x the forward.
+FLOP convention: forward 4*B*H*N^2*d, halved when causal (two N x N x d products); backward 2.5x
+the forward (five products). The dK/dV kernel performs four products (S, dP, dV, dK), i.e. 2x
+the forward's FLOPs; the dQ kernel recomputes S and dP and forms dQ (three products), work the
+backward figure above does not count.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -33,7 +36,7 @@ PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA: 256 CU x 2.4 GHz x 409
 HBM_PEAK_GBS = 8000.0
 METRIC = "attention fwd/bwd TFLOP/s + % bf16 MFMA peak (B2 H16 N4096 d64 causal)"
 WORKLOAD = "b2h16n4k_d64"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_main_b2h16n4k_d64_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_dkdv_b2h16n4k_d64_traffic.txt")
 BWD_SOURCE = os.path.join(ROOT, "exact_attention_94_amd", "csrc", "fa_bwd.hip")
 
 
@@ -80,8 +83,8 @@ def source_digest(path):
 
 
 def measured_traffic():
-    """HBM bytes per launch of the main backward kernel from the committed rocprofv3 counter
-    summary, or None when it is absent or was taken on a different kernel source."""
+    """HBM bytes per launch of the dK/dV kernel from the committed rocprofv3 counter summary, or
+    None when it is absent or was taken on a different kernel source."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     text = open(TRAFFIC_FILE, encoding="utf-8").read()
@@ -215,7 +218,8 @@ def main():
     f_fwd, f_bwd = flops(w)
     tf = lambda f, ms: f / (ms * 1e-3) / 1e12  # noqa: E731
     value = tf(f_fwd + f_bwd, step_ms)
-    main_tf = tf(f_bwd, main_ms)
+    f_dkdv = 2.0 * f_fwd  # S, dP, dV, dK
+    main_tf = tf(f_dkdv, main_ms)
     traffic = measured_traffic()
     out = {
         "metric": METRIC,
@@ -243,7 +247,7 @@ def main():
         "step_pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "host_wall_ms_per_step": round(1e3 * t_wall / K, 4),
         "roofline": {
-            "kernel": "bwd_main_kernel<64, bf16, f32 grads, causal>",
+            "kernel": "bwd_dkdv_kernel<64, bf16, f32 grads, causal>",
             "bound": "mfma",
             "achieved": round(main_tf, 2),
             "peak": PEAK_BF16_TFLOPS,
@@ -251,7 +255,7 @@ def main():
             "frac": round(main_tf / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "kernel_ms": round(main_ms, 4),
-            "flops_per_launch": f_bwd,
+            "flops_per_launch": f_dkdv,
         },
     }
     if not args.no_cpu_baseline:

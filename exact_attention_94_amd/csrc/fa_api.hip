@@ -20,6 +20,9 @@ fa_status check_shape(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
   const long long elems = (long long)B * H * N * d;
   if (elems > 0x7FFFFFFFLL) return FA_ERR_INVALID_ARG;
+  // Per-head byte offsets (and the prefetches a few tiles past N) must fit the 32-bit offsets
+  // of buffer loads.
+  if ((long long)N * d > (1LL << 30)) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
@@ -37,18 +40,17 @@ thread_local hipEvent_t t_prof_after = nullptr;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Workspace: D (fp32 [B,H,N], 256-byte aligned) | fp32 dQ accumulator [B,H,N,d] when the
-// gradients are 16-bit | fp16 copies of Q, K, V, dO ([B,H,N,d] each) when the inputs are bf16.
+// Workspace: D (fp32 [B,H,N]) | for bf16 inputs, fp16 copies of Q, K, V, dO ([B,H,N,d] each),
+// 256-byte aligned.
 struct WsLayout {
-  size_t dq_off, f16_off, total;
+  size_t f16_off, total;
 };
 
-WsLayout workspace_layout(int B, int H, int N, int d, fa_dtype in_dtype, fa_dtype grad_dtype) {
+WsLayout workspace_layout(int B, int H, int N, int d, fa_dtype in_dtype) {
   const size_t rows = (size_t)B * H * N;
   const size_t elems = rows * (size_t)d;
   WsLayout w;
-  w.dq_off = round_up(rows * sizeof(float), 256);
-  w.f16_off = round_up(w.dq_off + ((grad_dtype == FA_F32) ? 0 : elems * sizeof(float)), 256);
+  w.f16_off = round_up(rows * sizeof(float), 256);
   w.total = w.f16_off + ((in_dtype == FA_BF16) ? 4 * elems * 2 : 0);
   return w;
 }
@@ -99,7 +101,7 @@ size_t fa_backward_workspace_bytes(int B, int H, int N, int d, fa_dtype in_dtype
                                    fa_dtype grad_dtype) {
   if (check_shape(B, H, N, d) != FA_OK || !valid_dtype(in_dtype) || !valid_dtype(grad_dtype))
     return 0;
-  return workspace_layout(B, H, N, d, in_dtype, grad_dtype).total;
+  return workspace_layout(B, H, N, d, in_dtype).total;
 }
 
 fa_status fa_backward(const void* q, const void* k, const void* v, const void* o,
@@ -120,7 +122,7 @@ fa_status fa_backward(const void* q, const void* k, const void* v, const void* o
   if (in_dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   if (o_dtype != in_dtype && o_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
   if (grad_dtype != in_dtype && grad_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
-  const WsLayout ws = workspace_layout(B, H, N, d, in_dtype, grad_dtype);
+  const WsLayout ws = workspace_layout(B, H, N, d, in_dtype);
   if (!workspace || !aligned16(workspace) || workspace_bytes < ws.total) return FA_ERR_WORKSPACE;
   char* wsb = static_cast<char*>(workspace);
 
@@ -132,16 +134,16 @@ fa_status fa_backward(const void* q, const void* k, const void* v, const void* o
   a.dout = dout;
   a.lse = lse;
   a.delta = static_cast<float*>(workspace);
-  a.dq_acc = (grad_dtype == FA_F32) ? static_cast<float*>(dq)
-                                     : reinterpret_cast<float*>(wsb + ws.dq_off);
+  a.elems = (size_t)B * H * N * d;
   if (in_dtype == FA_BF16) {
-    const size_t elems = (size_t)B * H * N * d;
     uint16_t* f16 = reinterpret_cast<uint16_t*>(wsb + ws.f16_off);
+    a.ws16 = f16;
     a.q16 = f16;
-    a.k16 = f16 + elems;
-    a.v16 = f16 + 2 * elems;
-    a.do16 = f16 + 3 * elems;
+    a.k16 = f16 + a.elems;
+    a.v16 = f16 + 2 * a.elems;
+    a.do16 = f16 + 3 * a.elems;
   } else {
+    a.ws16 = nullptr;
     a.q16 = static_cast<const uint16_t*>(q);
     a.k16 = static_cast<const uint16_t*>(k);
     a.v16 = static_cast<const uint16_t*>(v);

@@ -124,11 +124,6 @@ __device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t byt
 __device__ __forceinline__ float buf_ldf(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
 }
-// fp32 atomic add (no return) through a buffer resource; out-of-range adds are dropped.
-__device__ __forceinline__ void buf_atomic_add(__amdgpu_buffer_rsrc_t r, uint32_t byte_off,
-                                               float v) {
-  __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, byte_off, 0, 0);
-}
 
 // s_waitcnt vmcnt(0) (expcnt / lgkmcnt left at their maxima): every outstanding vector memory
 // load of this wave has completed. Used once before a main loop so that no wait on loads issued

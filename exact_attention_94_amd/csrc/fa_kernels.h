@@ -26,28 +26,29 @@ struct BwdArgs {
   const void* o;
   const void* dout;
   const float* lse;
-  float* dq_acc;  // float32 [B,H,N,d] accumulator (the dq output itself when it is float32)
-  void* dq;       // dq output when its dtype is 16-bit (cast from dq_acc)
+  void* dq;
   void* dk;
   void* dv;
-  float* delta;   // float32 [B,H,N]: rowsum(dO * O)
-  // fp16 operands of the main kernel: the inputs themselves for fp16, copies made by the
-  // preprocess kernel (in the workspace) for bf16.
+  float* delta;  // float32 [B,H,N]: rowsum(dO * O)
+  // fp16 operands of the gradient kernels: the inputs themselves for fp16 inputs; for bf16
+  // inputs, the copies the preprocess kernel writes to ws16 (Q, K, V, dO, `elems` apart).
   const uint16_t* q16;
   const uint16_t* k16;
   const uint16_t* v16;
   const uint16_t* do16;
+  uint16_t* ws16;
+  size_t elems;  // B*H*N*d
   int N;
   int bh;
   int n_tiles;
   float scale;
-  float c;        // scale * log2(e)
+  float c;  // scale * log2(e)
 };
 
 // in_dtype / o_dtype / grad_dtype codes follow fa_dtype: 0 = f32, 1 = f16, 2 = bf16.
 hipError_t launch_forward(const FwdArgs& a, int d, int in_dtype, int o_f32, bool causal,
                           hipStream_t s);
-// ev_before / ev_after (may be null): recorded on `s` around the main backward kernel.
+// ev_before / ev_after (may be null): recorded on `s` around the dK/dV kernel.
 hipError_t launch_backward(const BwdArgs& a, int d, int in_dtype, int o_dtype, int grad_dtype,
                            bool causal, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after);
 

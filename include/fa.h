@@ -19,7 +19,8 @@
  * vectors are contiguous [B, H, N]. Q, K and V share N (self-attention). Pointers must be
  * device pointers (hipMalloc'd or equivalent) aligned to 16 bytes.
  *
- * Supported: d in {64, 128}; N >= 1 (a ragged tail is masked); B, H >= 1 with B*H*N*d < 2^31;
+ * Supported: d in {64, 128}; N >= 1 (a ragged tail is masked); B, H >= 1 with B*H*N*d < 2^31
+ * and N*d <= 2^30;
  * in_dtype in {FA_F32, FA_F16, FA_BF16}; any finite scale; causal in {0, 1}.
  * The backward supports in_dtype FA_F16 and FA_BF16.
  *
@@ -70,9 +71,9 @@ fa_status fa_forward(const void* q, const void* k, const void* v, void* o, float
 
 /*
  * Bytes of device workspace fa_backward needs for these sizes and dtypes: the row vector
- * D = rowsum(dO * O) (float32 [B,H,N]); when grad_dtype is not FA_F32, a float32 [B,H,N,d]
- * accumulator for dQ; when in_dtype is FA_BF16, fp16 copies of Q, K, V and dO (4 x [B,H,N,d]
- * 16-bit) used as the MFMA operands. Returns 0 for arguments fa_backward would reject.
+ * D = rowsum(dO * O) (float32 [B,H,N]) and, when in_dtype is FA_BF16, fp16 copies of Q, K, V and
+ * dO (4 x [B,H,N,d] 16-bit) used as the MFMA operands. grad_dtype does not change the size but is
+ * validated. Returns 0 for arguments fa_backward would reject.
  */
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d, fa_dtype in_dtype,
                                    fa_dtype grad_dtype);
@@ -89,9 +90,10 @@ size_t fa_backward_workspace_bytes(int B, int H, int N, int d, fa_dtype in_dtype
  *   workspace  device buffer of at least fa_backward_workspace_bytes(B,H,N,d,in_dtype,grad_dtype)
  *              bytes,
  *              16-byte aligned; contents on entry are ignored and clobbered
- * The three gradient products and the dP product use fp16 MFMA operands with fp32
- * accumulation (bf16 inputs are converted exactly while |x| >= 2^-14). dQ is accumulated
- * with float32 atomics, so its low bits may differ run to run; dK and dV are deterministic.
+ * Three kernels run on the stream: a row-wise preprocess (D, fp16 operand copies), a keys-outer
+ * kernel for dK and dV, and a queries-outer kernel for dQ. Every product uses fp16 MFMA operands
+ * with fp32 accumulation (bf16 inputs are converted exactly while |x| >= 2^-14). No atomics:
+ * all outputs are deterministic.
  */
 fa_status fa_backward(const void* q, const void* k, const void* v, const void* o,
                       const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
@@ -101,9 +103,9 @@ fa_status fa_backward(const void* q, const void* k, const void* v, const void* o
 
 /*
  * Profiling aid with no effect on results: after this call, every fa_backward call made by the
- * calling thread records `before` on its stream immediately before the main backward kernel is
- * launched and `after` immediately after it, so the caller can time that kernel alone with
- * hipEventElapsedTime. Both are hipEvent_t handles owned by the caller. Pass NULL, NULL to stop.
+ * calling thread records `before` on its stream immediately before its dK/dV kernel (the
+ * longest of its kernels) is launched and `after` immediately after it, so the caller can time
+ * that kernel alone with hipEventElapsedTime. Both are hipEvent_t handles owned by the caller. Pass NULL, NULL to stop.
  * Returns FA_ERR_INVALID_ARG if exactly one of them is NULL, FA_OK otherwise.
  */
 fa_status fa_profile_backward_main(void* before, void* after);

@@ -244,6 +244,7 @@ def test_repeat_determinism(fa):
     g1 = fa.backward(q, k, v, o1, do, l1, causal=True, grad_dtype=torch.float32)
     g2 = fa.backward(q, k, v, o1, do, l1, causal=True, grad_dtype=torch.float32)
     torch.cuda.synchronize()
+    # No atomics anywhere: every output is bitwise reproducible.
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
-    assert torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])
-    assert (g1[0] - g2[0]).abs().max().item() < 1e-5
+    for x, y in zip(g1, g2):
+        assert torch.equal(x, y)
