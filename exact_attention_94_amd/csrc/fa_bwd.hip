@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
   const int g = lane >> 5;
   const int r = lane & 31;
   const int N = a.N;
@@ -189,7 +189,8 @@ __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs 
       dkacc[db][i] = 0.f;
     }
 
-  const float c = a.c;
+  const float c = a.c;  // never 0 (the host maps scale 0 to a tiny value)
+  const float masked = c > 0.f ? -INFINITY : INFINITY;  // c * masked = -inf
   const int q_begin = CAUSAL ? (k0 / C::BQ) * C::BQ : 0;
   const int n_steps = (N - q_begin + C::BQ - 1) / C::BQ;  // >= 1 since k0 < N
 
@@ -254,8 +255,19 @@ __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs 
         pacc[qb] = mfma32x32x16<false>(da, vf[ks], pacc[qb]);
       }
     }
-    // P = exp2(c*S - LSE*log2e); dS = P * (dP - D). Slot i: query i0 + 32*qb + 16*(i/8) + 8*g + i%8.
-    const bool need_mask = (k0 + C::BKV > N) || (CAUSAL && (i0 < kw0 + 31));
+    // Mask (keys beyond N; causal: key after query) on the few tiles that need it, as a score of
+    // -inf after scaling. Slot i holds query i0 + 32*qb + 16*(i/8) + 8*g + i%8.
+    if ((k0 + C::BKV > N) || (CAUSAL && (i0 < kw0 + 31))) {
+#pragma unroll
+      for (int qb = 0; qb < C::QBS; ++qb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int q = i0 + qb * 32 + (i >> 3) * 16 + g * 8 + (i & 7);
+          const bool dead = (key >= N) || (CAUSAL && key > q);
+          sacc[qb][i] = dead ? masked : sacc[qb][i];
+        }
+    }
+    // P = exp2(c*S - LSE*log2e); dS = P * (dP - D).
     Frag16 pfr[C::QBS][2], dsf[C::QBS][2];
 #pragma unroll
     for (int qb = 0; qb < C::QBS; ++qb) {
@@ -271,11 +283,7 @@ __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs 
         for (int e = 0; e < 8; ++e) {
           const float lv = e < 4 ? l0[e] : l1[e - 4];
           const float dv = e < 4 ? d0[e] : d1[e - 4];
-          float pv = fast_exp2(__builtin_fmaf(sacc[qb][h * 8 + e], c, -lv));
-          if (need_mask) {
-            const bool dead = (key >= N) || (CAUSAL && key > i0 + qloc + e);
-            pv = dead ? 0.f : pv;
-          }
+          const float pv = fast_exp2(__builtin_fmaf(sacc[qb][h * 8 + e], c, -lv));
           p[e] = pv;
           ds[e] = pv * (pacc[qb][h * 8 + e] - dv);
         }
@@ -370,7 +378,7 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
   const int g = lane >> 5;
   const int r = lane & 31;
   const int N = a.N;
@@ -408,7 +416,8 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqacc[db][i] = 0.f;
 
-  const float c = a.c;
+  const float c = a.c;  // never 0 (the host maps scale 0 to a tiny value)
+  const float masked = c > 0.f ? -INFINITY : INFINITY;  // c * masked = -inf
   const int kv_end = CAUSAL ? min(N, qt0 + C::BR) : N;
   const int n_kt = (kv_end + C::BC - 1) / C::BC;
 
@@ -468,9 +477,19 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
         pacc[kb] = mfma32x32x16<false>(va, of[ks], pacc[kb]);
       }
     }
-    // dS^T = P^T * (dP^T - D), P = exp2(c*S - LSE*log2e). Slot i of block kb holds key
+    // Mask on the few tiles that need it. Slot i of block kb holds key
     // j0 + 32*kb + 16*(i/8) + 8*g + i%8.
-    const bool need_mask = (j0 + C::BC > N) || (CAUSAL && (j0 + C::BC - 1 > qw0));
+    if ((j0 + C::BC > N) || (CAUSAL && (j0 + C::BC - 1 > qw0))) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kk = j0 + kb * 32 + (i >> 3) * 16 + g * 8 + (i & 7);
+          const bool dead = (kk >= N) || (CAUSAL && kk > qrow);
+          sacc[kb][i] = dead ? masked : sacc[kb][i];
+        }
+    }
+    // dS^T = P^T * (dP^T - D), P = exp2(c*S - LSE*log2e).
     Frag16 dsf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -479,12 +498,7 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
         float ds[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          float pv = fast_exp2(__builtin_fmaf(sacc[kb][h * 8 + e], c, -lse2));
-          if (need_mask) {
-            const int kk = j0 + kb * 32 + h * 16 + g * 8 + e;
-            const bool dead = (kk >= N) || (CAUSAL && kk > qrow);
-            pv = dead ? 0.f : pv;
-          }
+          const float pv = fast_exp2(__builtin_fmaf(sacc[kb][h * 8 + e], c, -lse2));
           ds[e] = pv * (pacc[kb][h * 8 + e] - dlt);
         }
         dsf[kb][h].w = u32x4{pack2<false>(ds[0], ds[1]), pack2<false>(ds[2], ds[3]),
