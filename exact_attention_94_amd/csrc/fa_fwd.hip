@@ -223,10 +223,24 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
               for (int i = 0; i < 16; ++i) red = __builtin_fminf(red, sacc[kb][qb][i]);
             red = halves_min(red);
           }
-          const float m_blk = red * c;  // -inf when the whole tile is masked for this query
+            const float m_blk = red * c;  // -inf when the whole tile is masked for this query
+          // Exact running maximum: the largest weight of each row is then exp2(0) = 1, which
+          // bf16/fp16 hold exactly. (Deferring the rescale until the maximum grows by a margin
+          // saves the multiplies below but leaves that weight at 2^x with a rounding error of
+          // up to 2^-9, which measurably degrades O, and through D = rowsum(dO * O) the
+          // gradients, on peaked rows.)
           const float m_new = __builtin_fmaxf(m_run[qb], m_blk);
           const float corr = fast_exp2(m_run[qb] - m_new);
           m_run[qb] = m_new;
+          l_run[qb] *= corr;
+          // Rescale the accumulator only when some lane's maximum moved (corr == 1: identity).
+          if (__builtin_amdgcn_ballot_w64(corr != 1.f)) {
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) oacc[db][qb][i] *= corr;
+          }
+          const float m_ref = m_run[qb];
           float lsum = 0.f;
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
@@ -235,24 +249,17 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
               float p[8];
 #pragma unroll
               for (int e = 0; e < 8; ++e) {
-                p[e] = fast_exp2(__builtin_fmaf(sacc[kb][qb][h * 8 + e], c, -m_new));
-                lsum += p[e];
+                p[e] = fast_exp2(__builtin_fmaf(sacc[kb][qb][h * 8 + e], c, -m_ref));
+                lsum += p[e];  // fp32 row sum: the LSE needs it to well below bf16 precision
               }
               pf[kb][h][qb].w = u32x4{pack2<IS_BF16>(p[0], p[1]), pack2<IS_BF16>(p[2], p[3]),
                                       pack2<IS_BF16>(p[4], p[5]), pack2<IS_BF16>(p[6], p[7])};
             }
           }
-          l_run[qb] = l_run[qb] * corr + lsum;
-          // Rescale the accumulator only when some lane's maximum moved (corr == 1 is identity).
-          if (__builtin_amdgcn_ballot_w64(corr != 1.f)) {
-#pragma unroll
-            for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-              for (int i = 0; i < 16; ++i) oacc[db][qb][i] *= corr;
-          }
+          l_run[qb] += lsum;
         }
 
-        // ---- O^T += V^T P^T -----------------------------------------------------------------
+      // ---- O^T += V^T P^T -----------------------------------------------------------------
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
