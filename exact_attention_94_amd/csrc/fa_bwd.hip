@@ -136,7 +136,7 @@ struct Dkdv {
   static constexpr int QBS = BQ / 32;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int ROW = D + 8;     // Q / dO tile row stride (elements)
+  static constexpr int ROW = D + kLdsPad;     // Q / dO tile row stride (elements)
   static constexpr int TILE = BQ * ROW;
   static constexpr int STAGE = 2 * TILE + 2 * BQ * 2;  // Q, dO, then LSE*log2e and D (fp32)
   static constexpr int LDS_BYTES = 2 * STAGE * 2;
@@ -363,7 +363,7 @@ struct Dq {
   static constexpr int BC = 64;    // keys per K/V tile
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int ROW = D + 8;
+  static constexpr int ROW = D + kLdsPad;
   static constexpr int TILE = BC * ROW;
   static constexpr int STAGE = 2 * TILE;  // K then V
   static constexpr int LDS_BYTES = 2 * STAGE * 2;

@@ -15,6 +15,14 @@
 
 namespace fa {
 
+// Padding (in 16-bit elements) added to every row of a staged LDS tile, so that the 32 rows an
+// MFMA operand read touches start on different banks. Must keep rows 16-byte aligned.
+#ifndef FA_LDS_PAD
+#define FA_LDS_PAD 8
+#endif
+constexpr int kLdsPad = FA_LDS_PAD;
+static_assert(kLdsPad % 8 == 0, "LDS rows must stay 16-byte aligned");
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

@@ -56,15 +56,21 @@ __device__ __forceinline__ int krow_of_key(int kk) {
   return 8 * (2 * (kk >> 4) + ((kk >> 2) & 1)) + 4 * ((kk >> 3) & 1) + (kk & 3);
 }
 
+// Keys per K/V tile of the 16-bit forward kernel.
+#ifndef FA_FWD_BC
+#define FA_FWD_BC 64
+#endif
+
 template <int D, bool IS_BF16, bool O_F32, bool CAUSAL, int QB>
 struct Fwd16 {
   static constexpr int NW = 4;            // waves per workgroup
   static constexpr int NT = NW * 64;      // threads
   static constexpr int BR = NW * QB * 32; // query rows per workgroup
-  static constexpr int BC = 64;           // keys per K/V tile
+  static constexpr int BC = FA_FWD_BC;    // keys per K/V tile
+  static constexpr int KB = BC / 32;      // 32-key MFMA blocks per tile
   static constexpr int KS = D / 16;       // contraction steps of S^T = K Q^T
   static constexpr int DB = D / 32;       // 32-row blocks of O^T
-  static constexpr int KROW = D + 8;      // K and V tile row stride in LDS (elements)
+  static constexpr int KROW = D + kLdsPad;      // K and V tile row stride in LDS (elements)
   static constexpr int KTILE = BC * KROW;
   static constexpr int STAGE = 2 * KTILE;  // K then V, elements per LDS stage
   static constexpr int LDS_BYTES = 2 * STAGE * 2;
@@ -103,13 +109,17 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
   const int qw0 = qt0 + wave * QB * 32;  // first query of this wave
 
   // Q fragments (B operand of S^T = K Q^T): query qw0 + 32*qb + r, d = 16*ks + 8*g .. +8.
-  // Rows beyond N read as zeros.
+  // Rows beyond N read as zeros. A negative scale is folded into Q by flipping its sign bits
+  // (exact), so the math below only ever sees c = |scale| * log2(e) > 0 and a row maximum.
+  const uint32_t qsign = a.c < 0.f ? 0x80008000u : 0u;
   Frag16 qf[QB][C::KS];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
+    for (int ks = 0; ks < C::KS; ++ks) {
       qf[qb][ks].w = buf_ld16(qrs, (uint32_t)((qw0 + qb * 32 + r) * D + ks * 16 + g * 8) * 2);
+      qf[qb][ks].w ^= qsign;
+    }
 
   f32x16 oacc[C::DB][QB];
 #pragma unroll
@@ -125,9 +135,8 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
     l_run[qb] = 0.f;
   }
 
-  const float c = a.c;  // scale * log2(e); never 0 (the host maps scale 0 to a tiny value)
-  const bool c_pos = c > 0.f;
-  const float masked = c_pos ? -INFINITY : INFINITY;  // masked score: c * masked = -inf
+  // |scale| * log2(e); never 0 (the host maps scale 0 to a tiny value).
+  const float c = __builtin_fabsf(a.c);
 
   const int kv_end = CAUSAL ? min(N, qt0 + C::BR) : N;
   const int n_kt = (kv_end + C::BC - 1) / C::BC;
@@ -169,9 +178,9 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
         const uint16_t* vs_ = ks_ + C::KTILE;
 
         // ---- S^T = K Q^T ---------------------------------------------------------------
-        f32x16 sacc[2][QB];
+        f32x16 sacc[C::KB][QB];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -179,7 +188,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
+          for (int kb = 0; kb < C::KB; ++kb) {
             Frag16 kf;
             kf.w = *reinterpret_cast<const u32x4*>(ks_ + (kb * 32 + r) * C::KROW + ks * 16 + g * 8);
 #pragma unroll
@@ -195,35 +204,27 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
           for (int qb = 0; qb < QB; ++qb) {
             const int qrow = qw0 + qb * 32 + r;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
               for (int i = 0; i < 16; ++i) {
                 const int key = j0 + kb * 32 + (i >> 3) * 16 + g * 8 + (i & 7);
                 const bool dead = (key >= N) || (CAUSAL && key > qrow);
-                sacc[kb][qb][i] = dead ? masked : sacc[kb][qb][i];
+                sacc[kb][qb][i] = dead ? -INFINITY : sacc[kb][qb][i];
               }
           }
         }
 
         // ---- online softmax (log2 domain): m, l, corr per query (lane-local) ----------------
-        Frag16 pf[2][2][QB];
+        Frag16 pf[C::KB][2][QB];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           float red = sacc[0][qb][0];
-          if (c_pos) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-              for (int i = 0; i < 16; ++i) red = __builtin_fmaxf(red, sacc[kb][qb][i]);
-            red = halves_max(red);
-          } else {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-              for (int i = 0; i < 16; ++i) red = __builtin_fminf(red, sacc[kb][qb][i]);
-            red = halves_min(red);
-          }
-            const float m_blk = red * c;  // -inf when the whole tile is masked for this query
+            for (int i = 0; i < 16; ++i) red = __builtin_fmaxf(red, sacc[kb][qb][i]);
+          red = halves_max(red);
+          const float m_blk = red * c;  // -inf when the whole tile is masked for this query
           // Exact running maximum: the largest weight of each row is then exp2(0) = 1, which
           // bf16/fp16 hold exactly. (Deferring the rescale until the maximum grows by a margin
           // saves the multiplies below but leaves that weight at 2^x with a rounding error of
@@ -233,17 +234,16 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
           const float corr = fast_exp2(m_run[qb] - m_new);
           m_run[qb] = m_new;
           l_run[qb] *= corr;
-          // Rescale the accumulator only when some lane's maximum moved (corr == 1: identity).
-          if (__builtin_amdgcn_ballot_w64(corr != 1.f)) {
+          // Unconditional rescale: a branch here would split the tile's math into separate
+          // basic blocks and keep the scheduler from overlapping MFMA and VALU work.
 #pragma unroll
-            for (int db = 0; db < C::DB; ++db)
+          for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-              for (int i = 0; i < 16; ++i) oacc[db][qb][i] *= corr;
-          }
+            for (int i = 0; i < 16; ++i) oacc[db][qb][i] *= corr;
           const float m_ref = m_run[qb];
           float lsum = 0.f;
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
+          for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
               float p[8];
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
 
       // ---- O^T += V^T P^T -----------------------------------------------------------------
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
 #pragma unroll
