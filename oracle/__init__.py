@@ -1,4 +1,6 @@
 """Float64 CPU oracle for exact attention (test infrastructure only; see attention.py)."""
 from .attention import attn_bwd_ref, attn_fwd_ref, attn_rows_ref, attn_tiled_ref
+from .philox import dropout_keep_ref, keep_scale, keep_threshold, philox4x32
 
-__all__ = ["attn_fwd_ref", "attn_bwd_ref", "attn_tiled_ref", "attn_rows_ref"]
+__all__ = ["attn_fwd_ref", "attn_bwd_ref", "attn_tiled_ref", "attn_rows_ref", "philox4x32",
+           "keep_threshold", "keep_scale", "dropout_keep_ref"]

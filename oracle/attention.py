@@ -27,6 +27,9 @@ attn_tiled_ref  the blockwise online-softmax recurrence in the pages' V1 loop or
                 block, inner Q block), exposing the m / l / corr trajectory.
 attn_rows_ref   the forward for a chosen subset of query rows, one row at a time, O(N d) per row.
 
+The forward and backward take an optional dropout keep mask; philox.py generates it from a seed
+and an offset with the Philox-4x32-10 counter-based generator.
+
 Every function is pinned by tests that do not re-type its formula (see tests/test_oracle_pins.py):
 a printed worked trace, closed forms, invariants, finite differences and brute force.
 """
@@ -71,30 +74,45 @@ def _softmax_rows(s):
     return e / l[:, None], m, l
 
 
-def attn_fwd_ref(q, k, v, scale, causal):
+def _keep_heads(keep, G, N):
+    """Dropout keep mask as bool [G, N, N] (None -> None)."""
+    if keep is None:
+        return None
+    kp = np.asarray(keep, dtype=bool)
+    return kp.reshape((G, N, N))
+
+
+def attn_fwd_ref(q, k, v, scale, causal, keep=None, keep_scale=1.0):
     """Naive attention with S and P materialised per (b, h).
 
     q, k, v: [..., N, d] (any real dtype; upcast to float64).
     Returns (O [..., N, d] float64, LSE [..., N] float64) where LSE = m + log(l) is the natural-log
     logsumexp of the *scaled* scores ([FA-why] §03 3.2: m + log l is the logsumexp).
     [FA-V1] §2.2 steps 1-3: S = QK^T, P = softmax(S), O = PV.
+
+    Dropout ([FA-why] §05, fourth difference): with a keep mask Z ([..., N, N] bool) the output
+    is O = (P * Z * keep_scale) V, applied to the normalised probabilities; LSE stays that of the
+    undropped softmax (it only normalises P).
     """
     qh, lead = _heads(q)
     kh, _ = _heads(k)
     vh, _ = _heads(v)
     G, N, _ = qh.shape
     dv = vh.shape[-1]
+    kp = _keep_heads(keep, G, N)
     o = np.empty((G, N, dv))
     lse = np.empty((G, N))
     for g in range(G):
         s = _scores(qh[g], kh[g], scale, causal)
         p, m, l = _softmax_rows(s)
+        if kp is not None:
+            p = np.where(kp[g], p * keep_scale, 0.0)
         o[g] = p @ vh[g]
         lse[g] = m + np.log(l)
     return o.reshape(lead + (N, dv)), lse.reshape(lead + (N,))
 
 
-def attn_bwd_ref(q, k, v, do, scale, causal, o=None):
+def attn_bwd_ref(q, k, v, do, scale, causal, o=None, keep=None, keep_scale=1.0):
     """Naive backward of O = softmax(scale*Q K^T) V with the upstream gradient dO.
 
     [FA-why] §03 3.3: with G = dO and A = G V^T = dL/dP,
@@ -102,9 +120,13 @@ def attn_bwd_ref(q, k, v, do, scale, causal, o=None):
         dQ = dS K * scale,  dK = dS^T Q * scale,  dV = P^T G
     where the page's 1/sqrt(d) is the softmax scale (here an explicit argument).
 
+    With a dropout keep mask Z (same mask as the forward, regenerated from seed and offset,
+    [FA-why] §05): O = P_d V with P_d = P * Z * keep_scale, so by the chain rule
+        dV = P_d^T G,  A = (G V^T) * Z * keep_scale = dL/dP,  and dS, dQ, dK as above.
+
     Returns dict with dq, dk, dv ([..., N, d]) and D = rowsum(dP * P) ([..., N]).
     If `o` (the forward output) is given, also returns D_o = rowsum(dO * O), which equals D in
-    real arithmetic; callers compare the two.
+    real arithmetic (with or without dropout); callers compare the two.
     """
     qh, lead = _heads(q)
     kh, _ = _heads(k)
@@ -115,11 +137,16 @@ def attn_bwd_ref(q, k, v, do, scale, causal, o=None):
     dk = np.empty_like(qh)
     dv = np.empty_like(qh)
     D = np.empty((G, N))
+    kp = _keep_heads(keep, G, N)
     for g in range(G):
         s = _scores(qh[g], kh[g], scale, causal)
         p, _, _ = _softmax_rows(s)
-        dv[g] = p.T @ doh[g]
-        dp = doh[g] @ vh[g].T
+        if kp is None:
+            dv[g] = p.T @ doh[g]
+            dp = doh[g] @ vh[g].T
+        else:
+            dv[g] = np.where(kp[g], p * keep_scale, 0.0).T @ doh[g]
+            dp = np.where(kp[g], (doh[g] @ vh[g].T) * keep_scale, 0.0)
         D[g] = (dp * p).sum(axis=1)
         ds = p * (dp - D[g][:, None])
         dq[g] = scale * (ds @ kh[g])
