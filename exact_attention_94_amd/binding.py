@@ -18,8 +18,8 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = ra
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_forward", "fa_backward", "fa_backward_workspace_bytes", "fa_profile_backward_main",
-           "fa_status_string")
+EXPORTS = ("fa_forward", "fa_forward_dropout", "fa_backward", "fa_backward_dropout",
+           "fa_backward_workspace_bytes", "fa_profile_backward_main", "fa_status_string")
 
 _lib = None
 
@@ -44,11 +44,17 @@ def load(path=LIB_PATH):
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, vp]
     lib.fa_forward.restype = i
+    u64, u32 = ctypes.c_uint64, ctypes.c_uint32
+    lib.fa_forward_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, f, u64, u32, vp]
+    lib.fa_forward_dropout.restype = i
     lib.fa_backward_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_backward_workspace_bytes.restype = sz
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, i,
                                 vp, sz, vp]
     lib.fa_backward.restype = i
+    lib.fa_backward_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i,
+                                        i, f, u64, u32, vp, sz, vp]
+    lib.fa_backward_dropout.restype = i
     lib.fa_profile_backward_main.argtypes = [vp, vp]
     lib.fa_profile_backward_main.restype = i
     lib.fa_status_string.argtypes = [i]
@@ -89,11 +95,13 @@ def _stream(t):
     return ctypes.c_void_p(_torch().cuda.current_stream(t.device).cuda_stream)
 
 
-def forward(q, k, v, scale=None, causal=False, o_dtype=None, out=None, lse=None):
+def forward(q, k, v, scale=None, causal=False, o_dtype=None, out=None, lse=None,
+            dropout_p=None, seed=0, offset=0):
     """fa_forward on torch tensors [B, H, N, d]. Returns (O, LSE).
 
     scale defaults to 1/sqrt(d); o_dtype defaults to the input dtype (float32 is also allowed for
-    16-bit inputs). `out` / `lse` may be given to write into existing buffers.
+    16-bit inputs). `out` / `lse` may be given to write into existing buffers. With dropout_p
+    (not None) the call is fa_forward_dropout with that probability, `seed` and `offset`.
     """
     torch = _torch()
     _check_bhnd("q", q)
@@ -110,11 +118,16 @@ def forward(q, k, v, scale=None, causal=False, o_dtype=None, out=None, lse=None)
         _check_bhnd("out", out, q.shape)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    st = load().fa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                           lse.data_ptr(), B, H, N, d, scale, int(bool(causal)),
-                           dtype_code(q.dtype), dtype_code(out.dtype), _stream(q))
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+            scale, int(bool(causal)), dtype_code(q.dtype), dtype_code(out.dtype))
+    if dropout_p is None:
+        st = load().fa_forward(*args, _stream(q))
+        where = "fa_forward"
+    else:
+        st = load().fa_forward_dropout(*args, float(dropout_p), int(seed), int(offset), _stream(q))
+        where = "fa_forward_dropout"
     if st != FA_OK:
-        raise FAError(st, "fa_forward")
+        raise FAError(st, where)
     return out, lse
 
 
@@ -131,11 +144,12 @@ def workspace_bytes(B, H, N, d, in_dtype_code, grad_dtype_code):
 
 
 def backward(q, k, v, o, dout, lse, scale=None, causal=False, grad_dtype=None, workspace=None,
-             grads=None):
+             grads=None, dropout_p=None, seed=0, offset=0):
     """fa_backward on torch tensors. Returns (dQ, dK, dV) in grad_dtype (default: q.dtype).
 
     `workspace` (a uint8 GPU tensor) is allocated when not given; `grads` may supply the three
-    output tensors.
+    output tensors. With dropout_p (not None) the call is fa_backward_dropout, which regenerates
+    the forward's keep mask from the same (dropout_p, seed, offset).
     """
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
@@ -151,11 +165,16 @@ def backward(q, k, v, o, dout, lse, scale=None, causal=False, grad_dtype=None, w
     need = workspace_bytes(B, H, N, d, dtype_code(q.dtype), gcode)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    st = load().fa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                            dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                            dv.data_ptr(), B, H, N, d, scale, int(bool(causal)),
-                            dtype_code(q.dtype), dtype_code(o.dtype), gcode,
-                            workspace.data_ptr(), workspace.numel(), _stream(q))
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, scale,
+            int(bool(causal)), dtype_code(q.dtype), dtype_code(o.dtype), gcode)
+    if dropout_p is None:
+        st = load().fa_backward(*args, workspace.data_ptr(), workspace.numel(), _stream(q))
+        where = "fa_backward"
+    else:
+        st = load().fa_backward_dropout(*args, float(dropout_p), int(seed), int(offset),
+                                        workspace.data_ptr(), workspace.numel(), _stream(q))
+        where = "fa_backward_dropout"
     if st != FA_OK:
-        raise FAError(st, "fa_backward")
+        raise FAError(st, where)
     return dq, dk, dv

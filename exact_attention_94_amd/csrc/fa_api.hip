@@ -40,6 +40,20 @@ thread_local hipEvent_t t_prof_after = nullptr;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Dropout parameters: keep threshold T = floor((1 - p) * 65536 + 1/2) over 16-bit random values
+// and the multiplier 65536 / T of kept probabilities. p must be finite and in [0, 1).
+bool make_drop(float p, uint64_t seed, uint32_t offset, fa::DropParams& dp) {
+  if (!(p >= 0.f && p < 1.f)) return false;
+  const double t = floor((1.0 - (double)p) * 65536.0 + 0.5);
+  if (t < 1.0) return false;  // p so close to 1 that nothing would be kept
+  dp.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
+  dp.seed_hi = (uint32_t)(seed >> 32);
+  dp.offset = offset;
+  dp.keep_t = (uint32_t)t;
+  dp.keep_scale = (float)(65536.0 / t);
+  return true;
+}
+
 // Workspace: D (fp32 [B,H,N]) | for bf16 inputs, fp16 copies of Q, K, V, dO ([B,H,N,d] each),
 // 256-byte aligned.
 struct WsLayout {
@@ -70,9 +84,13 @@ const char* fa_status_string(fa_status s) {
   return "unknown fa_status";
 }
 
-fa_status fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                     int H, int N, int d, float scale, int causal, fa_dtype in_dtype,
-                     fa_dtype o_dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+fa_status forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                       int H, int N, int d, float scale, int causal, fa_dtype in_dtype,
+                       fa_dtype o_dtype, const fa::DropParams* drop, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_INVALID_ARG;
@@ -82,8 +100,10 @@ fa_status fa_forward(const void* q, const void* k, const void* v, void* o, float
   const fa_status st = check_shape(B, H, N, d);
   if (st != FA_OK) return st;
   if (o_dtype != in_dtype && o_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if (drop && in_dtype == FA_F32) return FA_ERR_UNSUPPORTED;
 
   fa::FwdArgs a{};
+  if (drop) a.drop = *drop;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -93,22 +113,16 @@ fa_status fa_forward(const void* q, const void* k, const void* v, void* o, float
   a.bh = B * H;
   a.c = log2_scale(scale);
   const hipError_t e = fa::launch_forward(a, d, (int)in_dtype, o_dtype == FA_F32 ? 1 : 0,
-                                          causal != 0, static_cast<hipStream_t>(stream));
+                                          causal != 0, drop != nullptr,
+                                          static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-size_t fa_backward_workspace_bytes(int B, int H, int N, int d, fa_dtype in_dtype,
-                                   fa_dtype grad_dtype) {
-  if (check_shape(B, H, N, d) != FA_OK || !valid_dtype(in_dtype) || !valid_dtype(grad_dtype))
-    return 0;
-  return workspace_layout(B, H, N, d, in_dtype).total;
-}
-
-fa_status fa_backward(const void* q, const void* k, const void* v, const void* o,
-                      const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
-                      int H, int N, int d, float scale, int causal, fa_dtype in_dtype,
-                      fa_dtype o_dtype, fa_dtype grad_dtype, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+fa_status backward_impl(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                        int H, int N, int d, float scale, int causal, fa_dtype in_dtype,
+                        fa_dtype o_dtype, fa_dtype grad_dtype, const fa::DropParams* drop,
+                        void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
       !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
@@ -156,10 +170,61 @@ fa_status fa_backward(const void* q, const void* k, const void* v, const void* o
   a.bh = B * H;
   a.scale = scale;
   a.c = log2_scale(scale);
+  if (drop) a.drop = *drop;
   const hipError_t e = fa::launch_backward(a, d, (int)in_dtype, (int)o_dtype, (int)grad_dtype,
-                                           causal != 0, static_cast<hipStream_t>(stream),
-                                           t_prof_before, t_prof_after);
+                                           causal != 0, drop != nullptr,
+                                           static_cast<hipStream_t>(stream), t_prof_before,
+                                           t_prof_after);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int H, int N, int d, float scale, int causal, fa_dtype in_dtype,
+                     fa_dtype o_dtype, void* stream) {
+  return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, in_dtype, o_dtype, nullptr,
+                      stream);
+}
+
+fa_status fa_forward_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int H, int N, int d, float scale, int causal,
+                             fa_dtype in_dtype, fa_dtype o_dtype, float dropout_p, uint64_t seed,
+                             uint32_t offset, void* stream) {
+  fa::DropParams dp{};
+  if (!make_drop(dropout_p, seed, offset, dp)) return FA_ERR_INVALID_ARG;
+  return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, in_dtype, o_dtype, &dp,
+                      stream);
+}
+
+size_t fa_backward_workspace_bytes(int B, int H, int N, int d, fa_dtype in_dtype,
+                                   fa_dtype grad_dtype) {
+  if (check_shape(B, H, N, d) != FA_OK || !valid_dtype(in_dtype) || !valid_dtype(grad_dtype))
+    return 0;
+  return workspace_layout(B, H, N, d, in_dtype).total;
+}
+
+fa_status fa_backward(const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                      int H, int N, int d, float scale, int causal, fa_dtype in_dtype,
+                      fa_dtype o_dtype, fa_dtype grad_dtype, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, in_dtype,
+                       o_dtype, grad_dtype, nullptr, workspace, workspace_bytes, stream);
+}
+
+fa_status fa_backward_dropout(const void* q, const void* k, const void* v, const void* o,
+                              const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                              int B, int H, int N, int d, float scale, int causal,
+                              fa_dtype in_dtype, fa_dtype o_dtype, fa_dtype grad_dtype,
+                              float dropout_p, uint64_t seed, uint32_t offset, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  fa::DropParams dp{};
+  if (!make_drop(dropout_p, seed, offset, dp)) return FA_ERR_INVALID_ARG;
+  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, in_dtype,
+                       o_dtype, grad_dtype, &dp, workspace, workspace_bytes, stream);
 }
 
 fa_status fa_profile_backward_main(void* before, void* after) {

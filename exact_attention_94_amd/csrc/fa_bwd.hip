@@ -142,9 +142,11 @@ struct Dkdv {
   static constexpr int LDS_BYTES = 2 * STAGE * 2;
   static constexpr int CHUNKS = BQ * D / 8 / NT;  // 16-byte chunks per thread per tile
   static constexpr int MIN_WG = (D == 64) ? 2 : 1;
+  // Dropout instances: one 32-bit keep word per (wave, query of the step) after the stages.
+  static constexpr int MASK_BYTES = 4 * BQ * 4;
 };
 
-template <int D, bool IS_BF16, bool G_F32, bool CAUSAL>
+template <int D, bool IS_BF16, bool G_F32, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs a) {
   using C = Dkdv<D>;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
@@ -267,7 +269,24 @@ __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs 
           sacc[qb][i] = dead ? masked : sacc[qb][i];
         }
     }
-    // P = exp2(c*S - LSE*log2e); dS = P * (dP - D).
+    // Dropout: the keep bits of (query i0 + lane, this wave's 32 keys) come from four Philox
+    // blocks of 8 keys; lane (g, r) needs bit r of the words of its own queries, so the words
+    // go through this wave's slice of LDS (written and read by the same wave, in order).
+    uint32_t* mask_w = nullptr;
+    if constexpr (DROP) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int kg = 0; kg < 4; ++kg)
+        word |= keep_bits8(a.drop, (uint32_t)(kw0 >> 3) + kg, (uint32_t)(i0 + lane), (uint32_t)bh)
+                << (8 * kg);
+      mask_w = reinterpret_cast<uint32_t*>(smem + 2 * C::STAGE) + wave * C::BQ;
+      mask_w[lane] = word;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    // P = exp2(c*S - LSE*log2e); dS = P * (dP - D). With dropout, dV takes the kept P scaled
+    // by 1 / keep rate, and dP = (dO V^T) * keep / keep rate.
     Frag16 pfr[C::QBS][2], dsf[C::QBS][2];
 #pragma unroll
     for (int qb = 0; qb < C::QBS; ++qb) {
@@ -278,14 +297,27 @@ __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs 
         const f32x4 l1 = *reinterpret_cast<const f32x4*>(lse_s + qloc + 4);
         const f32x4 d0 = *reinterpret_cast<const f32x4*>(del_s + qloc);
         const f32x4 d1 = *reinterpret_cast<const f32x4*>(del_s + qloc + 4);
+        u32x4 mw0 = u32x4{0, 0, 0, 0}, mw1 = u32x4{0, 0, 0, 0};
+        if constexpr (DROP) {
+          mw0 = *reinterpret_cast<const u32x4*>(mask_w + qloc);
+          mw1 = *reinterpret_cast<const u32x4*>(mask_w + qloc + 4);
+        }
         float p[8], ds[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float lv = e < 4 ? l0[e] : l1[e - 4];
           const float dv = e < 4 ? d0[e] : d1[e - 4];
           const float pv = fast_exp2(__builtin_fmaf(sacc[qb][h * 8 + e], c, -lv));
-          p[e] = pv;
-          ds[e] = pv * (pacc[qb][h * 8 + e] - dv);
+          if constexpr (DROP) {
+            const uint32_t w = e < 4 ? mw0[e] : mw1[e - 4];
+            const bool keep = (w >> r) & 1u;
+            const float ks = a.drop.keep_scale;
+            p[e] = keep ? pv * ks : 0.f;
+            ds[e] = pv * ((keep ? pacc[qb][h * 8 + e] * ks : 0.f) - dv);
+          } else {
+            p[e] = pv;
+            ds[e] = pv * (pacc[qb][h * 8 + e] - dv);
+          }
         }
         pfr[qb][h].w = u32x4{pack2<false>(p[0], p[1]), pack2<false>(p[2], p[3]),
                              pack2<false>(p[4], p[5]), pack2<false>(p[6], p[7])};
@@ -371,7 +403,7 @@ struct Dq {
   static constexpr int MIN_WG = (D == 64) ? 2 : 1;
 };
 
-template <int D, bool IS_BF16, bool G_F32, bool CAUSAL>
+template <int D, bool IS_BF16, bool G_F32, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
   using C = Dq<D>;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
@@ -489,17 +521,27 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
           sacc[kb][i] = dead ? masked : sacc[kb][i];
         }
     }
-    // dS^T = P^T * (dP^T - D), P = exp2(c*S - LSE*log2e).
+    // dS^T = P^T * (dP^T - D), P = exp2(c*S - LSE*log2e); with dropout dP is (dO V^T) * keep /
+    // keep rate, the keep bits of this lane's 8 keys coming from one Philox block.
     Frag16 dsf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
+        uint32_t bits = 0xFFu;
+        if constexpr (DROP)
+          bits = keep_bits8(a.drop, (uint32_t)(j0 + kb * 32 + h * 16 + g * 8) >> 3,
+                            (uint32_t)qrow, (uint32_t)bh);
         float ds[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float pv = fast_exp2(__builtin_fmaf(sacc[kb][h * 8 + e], c, -lse2));
-          ds[e] = pv * (pacc[kb][h * 8 + e] - dlt);
+          if constexpr (DROP) {
+            const float dp = ((bits >> e) & 1u) ? pacc[kb][h * 8 + e] * a.drop.keep_scale : 0.f;
+            ds[e] = pv * (dp - dlt);
+          } else {
+            ds[e] = pv * (pacc[kb][h * 8 + e] - dlt);
+          }
         }
         dsf[kb][h].w = u32x4{pack2<false>(ds[0], ds[1]), pack2<false>(ds[2], ds[3]),
                              pack2<false>(ds[4], ds[5]), pack2<false>(ds[6], ds[7])};
@@ -573,42 +615,51 @@ static hipError_t launch_dyn(K kern, int grid, int lds, BwdArgs a, hipStream_t s
   return hipGetLastError();
 }
 
-template <int D, bool IS_BF16, bool G_F32, bool CAUSAL>
+template <int D, bool IS_BF16, bool G_F32, bool CAUSAL, bool DROP>
 static hipError_t launch_grads(BwdArgs a, hipStream_t s, hipEvent_t ev_before,
                                hipEvent_t ev_after) {
   hipError_t e;
   if (ev_before && (e = hipEventRecord(ev_before, s)) != hipSuccess) return e;
   a.n_tiles = (a.N + Dkdv<D>::BKV - 1) / Dkdv<D>::BKV;
-  e = launch_dyn(bwd_dkdv_kernel<D, IS_BF16, G_F32, CAUSAL>, a.n_tiles * a.bh, Dkdv<D>::LDS_BYTES,
-                 a, s);
+  e = launch_dyn(bwd_dkdv_kernel<D, IS_BF16, G_F32, CAUSAL, DROP>, a.n_tiles * a.bh,
+                 Dkdv<D>::LDS_BYTES + (DROP ? Dkdv<D>::MASK_BYTES : 0), a, s);
   if (e != hipSuccess) return e;
   if (ev_after && (e = hipEventRecord(ev_after, s)) != hipSuccess) return e;
   a.n_tiles = (a.N + Dq<D>::BR - 1) / Dq<D>::BR;
-  return launch_dyn(bwd_dq_kernel<D, IS_BF16, G_F32, CAUSAL>, a.n_tiles * a.bh, Dq<D>::LDS_BYTES,
-                    a, s);
+  return launch_dyn(bwd_dq_kernel<D, IS_BF16, G_F32, CAUSAL, DROP>, a.n_tiles * a.bh,
+                    Dq<D>::LDS_BYTES, a, s);
+}
+
+template <int D, bool IS_BF16, bool G_F32, bool DROP>
+static hipError_t launch_grads_c(const BwdArgs& a, bool causal, hipStream_t s,
+                                 hipEvent_t ev_before, hipEvent_t ev_after) {
+  return causal ? launch_grads<D, IS_BF16, G_F32, true, DROP>(a, s, ev_before, ev_after)
+                : launch_grads<D, IS_BF16, G_F32, false, DROP>(a, s, ev_before, ev_after);
 }
 
 template <int D, bool IS_BF16>
-static hipError_t launch_all(const BwdArgs& a, bool o_f32, bool g_f32, bool causal,
+static hipError_t launch_all(const BwdArgs& a, bool o_f32, bool g_f32, bool causal, bool drop,
                              hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after) {
   hipError_t e = launch_pre<D, IS_BF16>(a, o_f32, s);
   if (e != hipSuccess) return e;
   if (g_f32)
-    return causal ? launch_grads<D, IS_BF16, true, true>(a, s, ev_before, ev_after)
-                  : launch_grads<D, IS_BF16, true, false>(a, s, ev_before, ev_after);
-  return causal ? launch_grads<D, IS_BF16, false, true>(a, s, ev_before, ev_after)
-                : launch_grads<D, IS_BF16, false, false>(a, s, ev_before, ev_after);
+    return drop ? launch_grads_c<D, IS_BF16, true, true>(a, causal, s, ev_before, ev_after)
+                : launch_grads_c<D, IS_BF16, true, false>(a, causal, s, ev_before, ev_after);
+  return drop ? launch_grads_c<D, IS_BF16, false, true>(a, causal, s, ev_before, ev_after)
+              : launch_grads_c<D, IS_BF16, false, false>(a, causal, s, ev_before, ev_after);
 }
 
 hipError_t launch_backward(const BwdArgs& a, int d, int in_dtype, int o_dtype, int grad_dtype,
-                           bool causal, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after) {
+                           bool causal, bool drop, hipStream_t s, hipEvent_t ev_before,
+                           hipEvent_t ev_after) {
   const bool bf = in_dtype == 2;
   const bool o_f32 = o_dtype == 0;
   const bool g_f32 = grad_dtype == 0;
-  if (d == 64) return bf ? launch_all<64, true>(a, o_f32, g_f32, causal, s, ev_before, ev_after)
-                         : launch_all<64, false>(a, o_f32, g_f32, causal, s, ev_before, ev_after);
-  return bf ? launch_all<128, true>(a, o_f32, g_f32, causal, s, ev_before, ev_after)
-            : launch_all<128, false>(a, o_f32, g_f32, causal, s, ev_before, ev_after);
+  if (d == 64)
+    return bf ? launch_all<64, true>(a, o_f32, g_f32, causal, drop, s, ev_before, ev_after)
+              : launch_all<64, false>(a, o_f32, g_f32, causal, drop, s, ev_before, ev_after);
+  return bf ? launch_all<128, true>(a, o_f32, g_f32, causal, drop, s, ev_before, ev_after)
+            : launch_all<128, false>(a, o_f32, g_f32, causal, drop, s, ev_before, ev_after);
 }
 
 }  // namespace fa

@@ -143,6 +143,48 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Philox-4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as
+// 1, 2, 3", SC'11): each round takes the full 64-bit products M0*c0 and M1*c2 and maps
+// (c0, c1, c2, c3) to (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)); the key
+// advances by the Weyl increments between rounds.
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+  }
+  return u32x4{c0, c1, c2, c3};
+}
+
+// Dropout keep bits of one query and eight consecutive keys 8*group .. 8*group + 7 of head bh:
+// bit e is set iff the 16-bit value e of Philox(group, query, bh, offset; seed) is below
+// keep_t. The values are the output words' low and high halves in order w0.lo, w0.hi, w1.lo, ...
+struct DropParams {
+  uint32_t seed_lo, seed_hi, offset, keep_t;
+  float keep_scale;  // 65536 / keep_t
+};
+
+__device__ __forceinline__ uint32_t keep_bits8(const DropParams& dp, uint32_t group,
+                                               uint32_t query, uint32_t bh) {
+  const u32x4 w = philox4x32_10(group, query, bh, dp.offset, dp.seed_lo, dp.seed_hi);
+  uint32_t bits = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t v = (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu);
+    bits |= (v < dp.keep_t ? 1u : 0u) << e;
+  }
+  return bits;
+}
+
 // 16-byte global load / store helpers.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }

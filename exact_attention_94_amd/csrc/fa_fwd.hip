@@ -85,7 +85,7 @@ constexpr int fwd_qb() {
   return 1;
 }
 
-template <int D, bool IS_BF16, bool O_F32, bool CAUSAL, int QB>
+template <int D, bool IS_BF16, bool O_F32, bool CAUSAL, int QB, bool DROP>
 __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
   using C = Fwd16<D, IS_BF16, O_F32, CAUSAL, QB>;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
@@ -252,6 +252,16 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
                 p[e] = fast_exp2(__builtin_fmaf(sacc[kb][qb][h * 8 + e], c, -m_ref));
                 lsum += p[e];  // fp32 row sum: the LSE needs it to well below bf16 precision
               }
+              if constexpr (DROP) {
+                // Dropout on the probabilities that multiply V (the row sum above keeps every
+                // probability: the softmax is normalised before dropout). This lane's 8 keys
+                // form one aligned group of 8, i.e. one Philox block.
+                const uint32_t grp = (uint32_t)(j0 + kb * 32 + h * 16 + g * 8) >> 3;
+                const uint32_t bits = keep_bits8(a.drop, grp, (uint32_t)(qw0 + qb * 32 + r),
+                                                 (uint32_t)bh);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) p[e] = ((bits >> e) & 1u) ? p[e] : 0.f;
+              }
               pf[kb][h][qb].w = u32x4{pack2<IS_BF16>(p[0], p[1]), pack2<IS_BF16>(p[2], p[3]),
                                       pack2<IS_BF16>(p[4], p[5]), pack2<IS_BF16>(p[6], p[7])};
             }
@@ -309,7 +319,8 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
   for (int qb = 0; qb < QB; ++qb) {
     const int qrow = qw0 + qb * 32 + r;
     const float l_tot = halves_sum(l_run[qb]);
-    const float inv = 1.f / l_tot;
+    // With dropout, kept probabilities are scaled by 1 / keep rate.
+    const float inv = (DROP ? a.drop.keep_scale : 1.f) / l_tot;
     if (qrow < N) {
       if (g == 0) a.lse[(size_t)bh * N + qrow] = (m_run[qb] + fast_log2(l_tot)) * kLn2;
 #pragma unroll
@@ -471,12 +482,12 @@ __global__ __launch_bounds__(256, 2) void fwd32_kernel(FwdArgs a) {
 // ----------------------------------------------------------------------------------------
 // Host-side launchers (called by the C ABI after validation).
 // ----------------------------------------------------------------------------------------
-template <int D, bool IS_BF16, bool O_F32, bool CAUSAL, int QB>
+template <int D, bool IS_BF16, bool O_F32, bool CAUSAL, int QB, bool DROP>
 static hipError_t launch16(FwdArgs a, hipStream_t s) {
   using C = Fwd16<D, IS_BF16, O_F32, CAUSAL, QB>;
   a.n_tiles = (a.N + C::BR - 1) / C::BR;
   const int grid = a.n_tiles * a.bh;
-  auto kern = fwd16_kernel<D, IS_BF16, O_F32, CAUSAL, QB>;
+  auto kern = fwd16_kernel<D, IS_BF16, O_F32, CAUSAL, QB, DROP>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
   if (e != hipSuccess) return e;
@@ -485,10 +496,13 @@ static hipError_t launch16(FwdArgs a, hipStream_t s) {
 }
 
 template <int D, bool IS_BF16, bool O_F32>
-static hipError_t launch16_c(FwdArgs a, bool causal, hipStream_t s) {
+static hipError_t launch16_c(FwdArgs a, bool causal, bool drop, hipStream_t s) {
   constexpr int QB = fwd_qb<D>();
-  return causal ? launch16<D, IS_BF16, O_F32, true, QB>(a, s)
-                : launch16<D, IS_BF16, O_F32, false, QB>(a, s);
+  if (drop)
+    return causal ? launch16<D, IS_BF16, O_F32, true, QB, true>(a, s)
+                  : launch16<D, IS_BF16, O_F32, false, QB, true>(a, s);
+  return causal ? launch16<D, IS_BF16, O_F32, true, QB, false>(a, s)
+                : launch16<D, IS_BF16, O_F32, false, QB, false>(a, s);
 }
 
 template <int D>
@@ -504,15 +518,22 @@ static hipError_t launch32(FwdArgs a, bool causal, hipStream_t s) {
 }
 
 hipError_t launch_forward(const FwdArgs& a, int d, int in_dtype, int o_f32, bool causal,
-                          hipStream_t s) {
-  if (in_dtype == 0) return d == 64 ? launch32<64>(a, causal, s) : launch32<128>(a, causal, s);
+                          bool drop, hipStream_t s) {
+  if (in_dtype == 0) {
+    if (drop) return hipErrorInvalidValue;  // rejected by the C ABI before this point
+    return d == 64 ? launch32<64>(a, causal, s) : launch32<128>(a, causal, s);
+  }
   const bool bf = in_dtype == 2;
   if (d == 64) {
-    if (bf) return o_f32 ? launch16_c<64, true, true>(a, causal, s) : launch16_c<64, true, false>(a, causal, s);
-    return o_f32 ? launch16_c<64, false, true>(a, causal, s) : launch16_c<64, false, false>(a, causal, s);
+    if (bf) return o_f32 ? launch16_c<64, true, true>(a, causal, drop, s)
+                         : launch16_c<64, true, false>(a, causal, drop, s);
+    return o_f32 ? launch16_c<64, false, true>(a, causal, drop, s)
+                 : launch16_c<64, false, false>(a, causal, drop, s);
   }
-  if (bf) return o_f32 ? launch16_c<128, true, true>(a, causal, s) : launch16_c<128, true, false>(a, causal, s);
-  return o_f32 ? launch16_c<128, false, true>(a, causal, s) : launch16_c<128, false, false>(a, causal, s);
+  if (bf) return o_f32 ? launch16_c<128, true, true>(a, causal, drop, s)
+                       : launch16_c<128, true, false>(a, causal, drop, s);
+  return o_f32 ? launch16_c<128, false, true>(a, causal, drop, s)
+               : launch16_c<128, false, false>(a, causal, drop, s);
 }
 
 }  // namespace fa

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "fa_device.h"
+
 namespace fa {
 
 struct FwdArgs {
@@ -17,6 +19,7 @@ struct FwdArgs {
   int bh;       // B * H
   int n_tiles;  // query tiles per head (set by the launcher)
   float c;      // scale * log2(e), never 0
+  DropParams drop;  // used only by the dropout instances
 };
 
 struct BwdArgs {
@@ -43,13 +46,16 @@ struct BwdArgs {
   int n_tiles;
   float scale;
   float c;  // scale * log2(e)
+  DropParams drop;  // used only by the dropout instances
 };
 
 // in_dtype / o_dtype / grad_dtype codes follow fa_dtype: 0 = f32, 1 = f16, 2 = bf16.
+// dropout: run the instances that apply the keep mask of a.drop (16-bit inputs only).
 hipError_t launch_forward(const FwdArgs& a, int d, int in_dtype, int o_f32, bool causal,
-                          hipStream_t s);
+                          bool dropout, hipStream_t s);
 // ev_before / ev_after (may be null): recorded on `s` around the dK/dV kernel.
 hipError_t launch_backward(const BwdArgs& a, int d, int in_dtype, int o_dtype, int grad_dtype,
-                           bool causal, hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after);
+                           bool causal, bool dropout, hipStream_t s, hipEvent_t ev_before,
+                           hipEvent_t ev_after);
 
 }  // namespace fa

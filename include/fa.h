@@ -39,6 +39,7 @@
 #define FA_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -100,6 +101,40 @@ fa_status fa_backward(const void* q, const void* k, const void* v, const void* o
                       int H, int N, int d, float scale, int causal, fa_dtype in_dtype,
                       fa_dtype o_dtype, fa_dtype grad_dtype, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * Forward pass with dropout on the attention probabilities ("FlashAttention 为什么不需要存下注意力矩阵"
+ * §05, fourth difference: the kernel keeps no mask, only the random generator's seed and
+ * offset, and the backward pass regenerates the same mask from them).
+ *
+ *   O = (P * Z / q) V  with P the softmax above, Z in {0, 1} the keep mask, q the keep rate;
+ *   LSE is that of the undropped softmax. Arguments as fa_forward, plus:
+ *   dropout_p  drop probability, finite, 0 <= p < 1 (otherwise FA_ERR_INVALID_ARG)
+ *   seed       64-bit generator key; offset  32-bit stream selector (e.g. a step counter)
+ * Mask: for head index bh = b*H + h, query i and key j, Philox-4x32-10 (Salmon et al., SC'11)
+ * with counter (j / 8, i, bh, offset) and key (seed low word, seed high word) yields eight 16-bit
+ * values (w0 low half, w0 high half, w1 low half, ... w3 high half) for keys 8*(j/8) .. +7;
+ * Z[i][j] = 1 iff the value for j is below T = floor((1 - p) * 65536 + 1/2), and q = T / 65536.
+ * The same (seed, offset) must be passed to fa_backward_dropout. in_dtype must be FA_F16 or
+ * FA_BF16 (FA_F32 returns FA_ERR_UNSUPPORTED).
+ */
+fa_status fa_forward_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int H, int N, int d, float scale, int causal,
+                             fa_dtype in_dtype, fa_dtype o_dtype, float dropout_p, uint64_t seed,
+                             uint32_t offset, void* stream);
+
+/*
+ * Backward pass of fa_forward_dropout, regenerating the same keep mask Z from (dropout_p, seed,
+ * offset): dV = (P * Z / q)^T dO, dP = (dO V^T) * Z / q, D = rowsum(dO * O), dS = P * (dP - D),
+ * dQ = scale * dS K, dK = scale * dS^T Q. Arguments, workspace and errors as fa_backward; o must
+ * be the dropout forward's output.
+ */
+fa_status fa_backward_dropout(const void* q, const void* k, const void* v, const void* o,
+                              const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                              int B, int H, int N, int d, float scale, int causal,
+                              fa_dtype in_dtype, fa_dtype o_dtype, fa_dtype grad_dtype,
+                              float dropout_p, uint64_t seed, uint32_t offset, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /*
  * Profiling aid with no effect on results: after this call, every fa_backward call made by the

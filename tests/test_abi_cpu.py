@@ -108,6 +108,43 @@ def test_backward_rejects(kw, status):
     assert bwd(**kw) == status
 
 
+def fwd_drop(p=0.1, seed=1, offset=0, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=3, N=100, d=64, scale=0.125, causal=1,
+             in_dtype=B.FA_BF16, o_dtype=B.FA_BF16)
+    a.update(kw)
+    return _lib().fa_forward_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                                     a["N"], a["d"], a["scale"], a["causal"], a["in_dtype"],
+                                     a["o_dtype"], p, seed, offset, None)
+
+
+def bwd_drop(p=0.1, seed=1, offset=0, **kw):
+    a = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=2, H=3, N=100, d=64,
+             scale=0.125, causal=1, in_dtype=B.FA_BF16, o_dtype=B.FA_F32, g_dtype=B.FA_F32,
+             ws=P, ws_bytes=1 << 30)
+    a.update(kw)
+    return _lib().fa_backward_dropout(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"],
+                                      a["dk"], a["dv"], a["B"], a["H"], a["N"], a["d"],
+                                      a["scale"], a["causal"], a["in_dtype"], a["o_dtype"],
+                                      a["g_dtype"], p, seed, offset, a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("p", [-0.1, 1.0, 1.5, float("nan"), float("inf"), 0.99999999])
+def test_dropout_rejects_bad_probability(p):
+    # 0.99999999 rounds to 1.0 in float32: nothing would be kept.
+    assert fwd_drop(p=p) == B.FA_ERR_INVALID_ARG
+    assert bwd_drop(p=p) == B.FA_ERR_INVALID_ARG
+
+
+def test_dropout_rejects_like_the_plain_calls():
+    assert fwd_drop(q=None) == B.FA_ERR_INVALID_ARG
+    assert fwd_drop(d=96) == B.FA_ERR_UNSUPPORTED
+    # The fp32 forward has no dropout instance.
+    assert fwd_drop(in_dtype=B.FA_F32, o_dtype=B.FA_F32) == B.FA_ERR_UNSUPPORTED
+    assert bwd_drop(ws=None) == B.FA_ERR_WORKSPACE
+    assert bwd_drop(in_dtype=B.FA_F32, o_dtype=B.FA_F32) == B.FA_ERR_UNSUPPORTED
+    assert bwd_drop(causal=3) == B.FA_ERR_INVALID_ARG
+
+
 def test_workspace_bytes():
     lib = _lib()
     ws = lib.fa_backward_workspace_bytes
