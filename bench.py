@@ -13,7 +13,10 @@ the forward (five products). The dK/dV kernel performs four products (S, dP, dV,
 the forward's FLOPs; the dQ kernel recomputes S and dP and forms dQ (three products), work the
 backward figure above does not count.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+The line also carries the same step with dropout p = 0.1 ("dropout": forward and backward times),
+which is not part of the headline value.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-dropout]
 """
 
 from __future__ import annotations
@@ -121,6 +124,42 @@ def cpu_baseline(w, t, heads=32):
                       f"divided by wall time"}
 
 
+def time_dropout(fa, ev, stream, w, q, k, v, do, o, lse, grads, ws, steps, p=0.1):
+    """The same step with dropout (keep mask regenerated from seed and offset in every kernel):
+    forward and backward times, reported beside the headline (which has no dropout)."""
+    import torch
+    f_fwd, f_bwd = flops(w)
+
+    def fwd(i):
+        fa.forward(q, k, v, scale=w.scale, causal=True, out=o, lse=lse, dropout_p=p, seed=77,
+                   offset=i)
+
+    def bwd(i):
+        fa.backward(q, k, v, o, do, lse, scale=w.scale, causal=True, grad_dtype=torch.float32,
+                    workspace=ws, grads=grads, dropout_p=p, seed=77, offset=i)
+
+    for i in range(2):
+        fwd(i)
+        bwd(i)
+    torch.cuda.synchronize()
+    e = [[ev.create() for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        ev.record(e[i][0], stream)
+        fwd(i)
+        ev.record(e[i][1], stream)
+        bwd(i)
+        ev.record(e[i][2], stream)
+    torch.cuda.synchronize()
+    fwd_ms = sum(ev.ms(x[0], x[1]) for x in e) / steps
+    bwd_ms = sum(ev.ms(x[1], x[2]) for x in e) / steps
+    for x in e:
+        for y in x:
+            ev.destroy(y)
+    return {"p": p, "steps": steps, "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+            "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
+            "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +167,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32)
+    ap.add_argument("--no-dropout", action="store_true",
+                    help="skip the extra timing of the dropout path (p = 0.1)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -258,6 +299,9 @@ def main():
             "flops_per_launch": f_dkdv,
         },
     }
+    if not args.no_dropout:
+        out["dropout"] = time_dropout(fa, ev, stream, w, q, k, v, do, o, lse, grads, ws,
+                                      steps=min(K, 10))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, t, heads=args.cpu_heads)
     print(json.dumps(out), flush=True)
