@@ -27,8 +27,9 @@ attn_tiled_ref  the blockwise online-softmax recurrence in the pages' V1 loop or
                 block, inner Q block), exposing the m / l / corr trajectory.
 attn_rows_ref   the forward for a chosen subset of query rows, one row at a time, O(N d) per row.
 
-The forward and backward take an optional dropout keep mask; philox.py generates it from a seed
-and an offset with the Philox-4x32-10 counter-based generator.
+The forward and backward take an optional dropout keep mask (philox.py generates it from a seed
+and an offset with the Philox-4x32-10 counter-based generator) and an optional visibility mask
+for block-sparse attention (block_mask_to_elements expands a tile mask to elements).
 
 Every function is pinned by tests that do not re-type its formula (see tests/test_oracle_pins.py):
 a printed worked trace, closed forms, invariants, finite differences and brute force.
@@ -38,7 +39,8 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["attn_fwd_ref", "attn_bwd_ref", "attn_tiled_ref", "attn_rows_ref"]
+__all__ = ["attn_fwd_ref", "attn_bwd_ref", "attn_tiled_ref", "attn_rows_ref",
+           "block_mask_to_elements"]
 
 
 def _heads(x):
@@ -49,29 +51,56 @@ def _heads(x):
     return x.reshape((-1,) + x.shape[-2:]), x.shape[:-2]
 
 
-def _scores(qh, kh, scale, causal):
+def _scores(qh, kh, scale, causal, visible=None):
     """S = scale * Q K^T for one head; with causal, key index j > query index i is -inf.
 
     [FA-V1] §2.2 step 1 (S = Q K^T, here with the softmax scale folded in, [FA-why] §03 3.3 uses
     1/sqrt(d)); the causal rule (masked score = -inf) is [FA-why] §03 3.2, last paragraph.
+    `visible` (bool [N, N], optional) masks further: scores of invisible keys are -inf.
     """
     s = scale * (qh @ kh.T)
     if causal:
         n_q, n_k = s.shape
         s[np.triu(np.ones((n_q, n_k), dtype=bool), 1)] = -np.inf
+    if visible is not None:
+        s[~np.asarray(visible, dtype=bool)] = -np.inf
     return s
+
+
+def _visible_heads(visible, G, N):
+    """Visibility mask as bool [G, N, N] (a single [N, N] mask applies to every head)."""
+    if visible is None:
+        return None
+    vm = np.asarray(visible, dtype=bool)
+    if vm.shape == (N, N):
+        return np.broadcast_to(vm, (G, N, N))
+    return vm.reshape((G, N, N))
 
 
 def _softmax_rows(s):
     """Safe softmax along each row: m = max, l = sum exp(s - m), P = exp(s - m) / l.
 
     [FA-why] §03 3.1 (subtract the row maximum, then normalise by the sum of exponentials).
+    A row whose scores are all -inf (no visible key, possible only with a block mask) gets
+    P = 0, m = -inf and l = 0, so that its output is 0 and its LSE = m + log l = -inf.
     Returns P, m, l.
     """
     m = s.max(axis=1)
-    e = np.exp(s - m[:, None])
+    empty = np.isneginf(m)
+    m_safe = np.where(empty, 0.0, m)
+    e = np.exp(s - m_safe[:, None])
     l = e.sum(axis=1)
-    return e / l[:, None], m, l
+    p = e / np.where(empty, 1.0, l)[:, None]
+    return p, m, l
+
+
+def block_mask_to_elements(block_mask, n, block):
+    """Element visibility [n, n] of a tile mask [ceil(n/block), ceil(n/block)]: query i may see
+    key j iff block_mask[i // block][j // block] is nonzero ([FA-why] §06: the whole-block skip of
+    the causal case, generalised to an arbitrary pattern of blocks, is block-sparse attention)."""
+    bm = np.asarray(block_mask) != 0
+    idx = np.arange(n) // block
+    return bm[np.ix_(idx, idx)]
 
 
 def _keep_heads(keep, G, N):
@@ -82,7 +111,7 @@ def _keep_heads(keep, G, N):
     return kp.reshape((G, N, N))
 
 
-def attn_fwd_ref(q, k, v, scale, causal, keep=None, keep_scale=1.0):
+def attn_fwd_ref(q, k, v, scale, causal, keep=None, keep_scale=1.0, visible=None):
     """Naive attention with S and P materialised per (b, h).
 
     q, k, v: [..., N, d] (any real dtype; upcast to float64).
@@ -93,6 +122,10 @@ def attn_fwd_ref(q, k, v, scale, causal, keep=None, keep_scale=1.0):
     Dropout ([FA-why] §05, fourth difference): with a keep mask Z ([..., N, N] bool) the output
     is O = (P * Z * keep_scale) V, applied to the normalised probabilities; LSE stays that of the
     undropped softmax (it only normalises P).
+
+    Block-sparse attention ([FA-why] §06): `visible` ([N, N] or [..., N, N] bool, see
+    block_mask_to_elements) hides keys from queries exactly like the causal rule; a query that
+    sees no key at all has O = 0 and LSE = -inf.
     """
     qh, lead = _heads(q)
     kh, _ = _heads(k)
@@ -100,19 +133,21 @@ def attn_fwd_ref(q, k, v, scale, causal, keep=None, keep_scale=1.0):
     G, N, _ = qh.shape
     dv = vh.shape[-1]
     kp = _keep_heads(keep, G, N)
+    vis = _visible_heads(visible, G, N)
     o = np.empty((G, N, dv))
     lse = np.empty((G, N))
     for g in range(G):
-        s = _scores(qh[g], kh[g], scale, causal)
+        s = _scores(qh[g], kh[g], scale, causal, None if vis is None else vis[g])
         p, m, l = _softmax_rows(s)
         if kp is not None:
             p = np.where(kp[g], p * keep_scale, 0.0)
         o[g] = p @ vh[g]
-        lse[g] = m + np.log(l)
+        with np.errstate(divide="ignore"):
+            lse[g] = m + np.log(l)
     return o.reshape(lead + (N, dv)), lse.reshape(lead + (N,))
 
 
-def attn_bwd_ref(q, k, v, do, scale, causal, o=None, keep=None, keep_scale=1.0):
+def attn_bwd_ref(q, k, v, do, scale, causal, o=None, keep=None, keep_scale=1.0, visible=None):
     """Naive backward of O = softmax(scale*Q K^T) V with the upstream gradient dO.
 
     [FA-why] §03 3.3: with G = dO and A = G V^T = dL/dP,
@@ -123,6 +158,9 @@ def attn_bwd_ref(q, k, v, do, scale, causal, o=None, keep=None, keep_scale=1.0):
     With a dropout keep mask Z (same mask as the forward, regenerated from seed and offset,
     [FA-why] §05): O = P_d V with P_d = P * Z * keep_scale, so by the chain rule
         dV = P_d^T G,  A = (G V^T) * Z * keep_scale = dL/dP,  and dS, dQ, dK as above.
+
+    With a block-sparse visibility mask (`visible`, as in attn_fwd_ref), invisible keys have
+    P = 0; a query that sees no key has zero gradients.
 
     Returns dict with dq, dk, dv ([..., N, d]) and D = rowsum(dP * P) ([..., N]).
     If `o` (the forward output) is given, also returns D_o = rowsum(dO * O), which equals D in
@@ -138,8 +176,9 @@ def attn_bwd_ref(q, k, v, do, scale, causal, o=None, keep=None, keep_scale=1.0):
     dv = np.empty_like(qh)
     D = np.empty((G, N))
     kp = _keep_heads(keep, G, N)
+    vis = _visible_heads(visible, G, N)
     for g in range(G):
-        s = _scores(qh[g], kh[g], scale, causal)
+        s = _scores(qh[g], kh[g], scale, causal, None if vis is None else vis[g])
         p, _, _ = _softmax_rows(s)
         if kp is None:
             dv[g] = p.T @ doh[g]
