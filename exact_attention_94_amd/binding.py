@@ -18,8 +18,11 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = ra
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_forward", "fa_forward_dropout", "fa_backward", "fa_backward_dropout",
-           "fa_backward_workspace_bytes", "fa_profile_backward_main", "fa_status_string")
+EXPORTS = ("fa_forward", "fa_forward_dropout", "fa_forward_blocksparse", "fa_backward",
+           "fa_backward_dropout", "fa_backward_blocksparse", "fa_backward_workspace_bytes",
+           "fa_profile_backward_main", "fa_status_string")
+
+SPARSE_BLOCK = 128  # queries x keys covered by one block-mask byte (FA_SPARSE_BLOCK)
 
 _lib = None
 
@@ -47,6 +50,8 @@ def load(path=LIB_PATH):
     u64, u32 = ctypes.c_uint64, ctypes.c_uint32
     lib.fa_forward_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, f, u64, u32, vp]
     lib.fa_forward_dropout.restype = i
+    lib.fa_forward_blocksparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, vp, i, vp]
+    lib.fa_forward_blocksparse.restype = i
     lib.fa_backward_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_backward_workspace_bytes.restype = sz
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, i,
@@ -55,6 +60,9 @@ def load(path=LIB_PATH):
     lib.fa_backward_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i,
                                         i, f, u64, u32, vp, sz, vp]
     lib.fa_backward_dropout.restype = i
+    lib.fa_backward_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i,
+                                            i, i, i, vp, i, vp, sz, vp]
+    lib.fa_backward_blocksparse.restype = i
     lib.fa_profile_backward_main.argtypes = [vp, vp]
     lib.fa_profile_backward_main.restype = i
     lib.fa_status_string.argtypes = [i]
@@ -95,13 +103,34 @@ def _stream(t):
     return ctypes.c_void_p(_torch().cuda.current_stream(t.device).cuda_stream)
 
 
+def _check_mask(block_mask, q):
+    B, H, N, _ = q.shape
+    nb = (N + SPARSE_BLOCK - 1) // SPARSE_BLOCK
+    if block_mask.dtype != _torch().uint8 or not block_mask.is_cuda:
+        raise TypeError("block_mask must be a uint8 GPU tensor")
+    if not block_mask.is_contiguous():
+        raise ValueError("block_mask must be contiguous")
+    if block_mask.dim() == 2:
+        heads = 1
+        shape = (nb, nb)
+    else:
+        heads = block_mask.shape[0]
+        shape = (heads, nb, nb)
+    if tuple(block_mask.shape) != shape or heads not in (1, B * H):
+        raise ValueError(f"block_mask has shape {tuple(block_mask.shape)}; expected [{nb}, {nb}] "
+                         f"or [1 or B*H, {nb}, {nb}]")
+    return heads
+
+
 def forward(q, k, v, scale=None, causal=False, o_dtype=None, out=None, lse=None,
-            dropout_p=None, seed=0, offset=0):
+            dropout_p=None, seed=0, offset=0, block_mask=None):
     """fa_forward on torch tensors [B, H, N, d]. Returns (O, LSE).
 
     scale defaults to 1/sqrt(d); o_dtype defaults to the input dtype (float32 is also allowed for
     16-bit inputs). `out` / `lse` may be given to write into existing buffers. With dropout_p
-    (not None) the call is fa_forward_dropout with that probability, `seed` and `offset`.
+    (not None) the call is fa_forward_dropout with that probability, `seed` and `offset`. With
+    block_mask (a uint8 GPU tensor [nb, nb] or [1 or B*H, nb, nb], nb = ceil(N / 128)) the call
+    is fa_forward_blocksparse.
     """
     torch = _torch()
     _check_bhnd("q", q)
@@ -120,7 +149,13 @@ def forward(q, k, v, scale=None, causal=False, o_dtype=None, out=None, lse=None,
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
             scale, int(bool(causal)), dtype_code(q.dtype), dtype_code(out.dtype))
-    if dropout_p is None:
+    if dropout_p is not None and block_mask is not None:
+        raise ValueError("dropout and a block mask cannot be combined")
+    if block_mask is not None:
+        heads = _check_mask(block_mask, q)
+        st = load().fa_forward_blocksparse(*args, block_mask.data_ptr(), heads, _stream(q))
+        where = "fa_forward_blocksparse"
+    elif dropout_p is None:
         st = load().fa_forward(*args, _stream(q))
         where = "fa_forward"
     else:
@@ -144,12 +179,13 @@ def workspace_bytes(B, H, N, d, in_dtype_code, grad_dtype_code):
 
 
 def backward(q, k, v, o, dout, lse, scale=None, causal=False, grad_dtype=None, workspace=None,
-             grads=None, dropout_p=None, seed=0, offset=0):
+             grads=None, dropout_p=None, seed=0, offset=0, block_mask=None):
     """fa_backward on torch tensors. Returns (dQ, dK, dV) in grad_dtype (default: q.dtype).
 
     `workspace` (a uint8 GPU tensor) is allocated when not given; `grads` may supply the three
     output tensors. With dropout_p (not None) the call is fa_backward_dropout, which regenerates
-    the forward's keep mask from the same (dropout_p, seed, offset).
+    the forward's keep mask from the same (dropout_p, seed, offset); with block_mask it is
+    fa_backward_blocksparse (the mask given to the forward).
     """
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
@@ -168,7 +204,14 @@ def backward(q, k, v, o, dout, lse, scale=None, causal=False, grad_dtype=None, w
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, scale,
             int(bool(causal)), dtype_code(q.dtype), dtype_code(o.dtype), gcode)
-    if dropout_p is None:
+    if dropout_p is not None and block_mask is not None:
+        raise ValueError("dropout and a block mask cannot be combined")
+    if block_mask is not None:
+        heads = _check_mask(block_mask, q)
+        st = load().fa_backward_blocksparse(*args, block_mask.data_ptr(), heads,
+                                            workspace.data_ptr(), workspace.numel(), _stream(q))
+        where = "fa_backward_blocksparse"
+    elif dropout_p is None:
         st = load().fa_backward(*args, workspace.data_ptr(), workspace.numel(), _stream(q))
         where = "fa_backward"
     else:

@@ -88,9 +88,23 @@ const char* fa_status_string(fa_status s) {
 
 namespace {
 
+// Block-sparse arguments: a device mask of mask_heads x nb x nb bytes, nb = ceil(N / 128),
+// mask_heads 1 or B*H; sequences up to 65536.
+fa_status check_sparse(const uint8_t* mask, int mask_heads, int B, int H, int N,
+                       fa::SparseParams& sp) {
+  if (!mask) return FA_ERR_INVALID_ARG;
+  if (mask_heads != 1 && (long long)mask_heads != (long long)B * H) return FA_ERR_INVALID_ARG;
+  if (N > fa::kSparseMaxN) return FA_ERR_UNSUPPORTED;
+  sp.mask = mask;
+  sp.mask_heads = mask_heads;
+  sp.nb = (N + fa::kSparseBlock - 1) / fa::kSparseBlock;
+  return FA_OK;
+}
+
 fa_status forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                        int H, int N, int d, float scale, int causal, fa_dtype in_dtype,
-                       fa_dtype o_dtype, const fa::DropParams* drop, void* stream) {
+                       fa_dtype o_dtype, const fa::DropParams* drop,
+                       const fa::SparseParams* sparse, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_INVALID_ARG;
@@ -100,10 +114,18 @@ fa_status forward_impl(const void* q, const void* k, const void* v, void* o, flo
   const fa_status st = check_shape(B, H, N, d);
   if (st != FA_OK) return st;
   if (o_dtype != in_dtype && o_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
-  if (drop && in_dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if ((drop || sparse) && in_dtype == FA_F32) return FA_ERR_UNSUPPORTED;
 
   fa::FwdArgs a{};
-  if (drop) a.drop = *drop;
+  fa::Mode mode = fa::Mode::kPlain;
+  if (drop) {
+    a.drop = *drop;
+    mode = fa::Mode::kDropout;
+  }
+  if (sparse) {
+    a.sparse = *sparse;
+    mode = fa::Mode::kSparse;
+  }
   a.q = q;
   a.k = k;
   a.v = v;
@@ -113,8 +135,7 @@ fa_status forward_impl(const void* q, const void* k, const void* v, void* o, flo
   a.bh = B * H;
   a.c = log2_scale(scale);
   const hipError_t e = fa::launch_forward(a, d, (int)in_dtype, o_dtype == FA_F32 ? 1 : 0,
-                                          causal != 0, drop != nullptr,
-                                          static_cast<hipStream_t>(stream));
+                                          causal != 0, mode, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -122,7 +143,8 @@ fa_status backward_impl(const void* q, const void* k, const void* v, const void*
                         const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
                         int H, int N, int d, float scale, int causal, fa_dtype in_dtype,
                         fa_dtype o_dtype, fa_dtype grad_dtype, const fa::DropParams* drop,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+                        const fa::SparseParams* sparse, void* workspace, size_t workspace_bytes,
+                        void* stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
       !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
@@ -170,11 +192,18 @@ fa_status backward_impl(const void* q, const void* k, const void* v, const void*
   a.bh = B * H;
   a.scale = scale;
   a.c = log2_scale(scale);
-  if (drop) a.drop = *drop;
+  fa::Mode mode = fa::Mode::kPlain;
+  if (drop) {
+    a.drop = *drop;
+    mode = fa::Mode::kDropout;
+  }
+  if (sparse) {
+    a.sparse = *sparse;
+    mode = fa::Mode::kSparse;
+  }
   const hipError_t e = fa::launch_backward(a, d, (int)in_dtype, (int)o_dtype, (int)grad_dtype,
-                                           causal != 0, drop != nullptr,
-                                           static_cast<hipStream_t>(stream), t_prof_before,
-                                           t_prof_after);
+                                           causal != 0, mode, static_cast<hipStream_t>(stream),
+                                           t_prof_before, t_prof_after);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -186,7 +215,7 @@ fa_status fa_forward(const void* q, const void* k, const void* v, void* o, float
                      int H, int N, int d, float scale, int causal, fa_dtype in_dtype,
                      fa_dtype o_dtype, void* stream) {
   return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, in_dtype, o_dtype, nullptr,
-                      stream);
+                      nullptr, stream);
 }
 
 fa_status fa_forward_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -196,7 +225,20 @@ fa_status fa_forward_dropout(const void* q, const void* k, const void* v, void* 
   fa::DropParams dp{};
   if (!make_drop(dropout_p, seed, offset, dp)) return FA_ERR_INVALID_ARG;
   return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, in_dtype, o_dtype, &dp,
-                      stream);
+                      nullptr, stream);
+}
+
+fa_status fa_forward_blocksparse(const void* q, const void* k, const void* v, void* o,
+                                 float* lse, int B, int H, int N, int d, float scale, int causal,
+                                 fa_dtype in_dtype, fa_dtype o_dtype, const uint8_t* block_mask,
+                                 int mask_heads, void* stream) {
+  fa::SparseParams sp{};
+  if (B >= 1 && H >= 1 && N >= 1) {
+    const fa_status st = check_sparse(block_mask, mask_heads, B, H, N, sp);
+    if (st != FA_OK) return st;
+  }
+  return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, in_dtype, o_dtype, nullptr,
+                      &sp, stream);
 }
 
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d, fa_dtype in_dtype,
@@ -212,7 +254,7 @@ fa_status fa_backward(const void* q, const void* k, const void* v, const void* o
                       fa_dtype o_dtype, fa_dtype grad_dtype, void* workspace,
                       size_t workspace_bytes, void* stream) {
   return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, in_dtype,
-                       o_dtype, grad_dtype, nullptr, workspace, workspace_bytes, stream);
+                       o_dtype, grad_dtype, nullptr, nullptr, workspace, workspace_bytes, stream);
 }
 
 fa_status fa_backward_dropout(const void* q, const void* k, const void* v, const void* o,
@@ -224,7 +266,22 @@ fa_status fa_backward_dropout(const void* q, const void* k, const void* v, const
   fa::DropParams dp{};
   if (!make_drop(dropout_p, seed, offset, dp)) return FA_ERR_INVALID_ARG;
   return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, in_dtype,
-                       o_dtype, grad_dtype, &dp, workspace, workspace_bytes, stream);
+                       o_dtype, grad_dtype, &dp, nullptr, workspace, workspace_bytes, stream);
+}
+
+fa_status fa_backward_blocksparse(const void* q, const void* k, const void* v, const void* o,
+                                  const void* dout, const float* lse, void* dq, void* dk,
+                                  void* dv, int B, int H, int N, int d, float scale, int causal,
+                                  fa_dtype in_dtype, fa_dtype o_dtype, fa_dtype grad_dtype,
+                                  const uint8_t* block_mask, int mask_heads, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  fa::SparseParams sp{};
+  if (B >= 1 && H >= 1 && N >= 1) {
+    const fa_status st = check_sparse(block_mask, mask_heads, B, H, N, sp);
+    if (st != FA_OK) return st;
+  }
+  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, in_dtype,
+                       o_dtype, grad_dtype, nullptr, &sp, workspace, workspace_bytes, stream);
 }
 
 fa_status fa_profile_backward_main(void* before, void* after) {

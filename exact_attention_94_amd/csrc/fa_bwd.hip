@@ -146,9 +146,10 @@ struct Dkdv {
   static constexpr int MASK_BYTES = 4 * BQ * 4;
 };
 
-template <int D, bool IS_BF16, bool G_F32, bool CAUSAL, bool DROP>
+template <int D, bool IS_BF16, bool G_F32, bool CAUSAL, bool DROP, bool SPARSE>
 __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs a) {
   using C = Dkdv<D>;
+  static_assert(!(DROP && SPARSE), "the dropout words and the sparse list share one LDS area");
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
   const int tid = threadIdx.x;
@@ -196,6 +197,29 @@ __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs 
   const int q_begin = CAUSAL ? (k0 / C::BQ) * C::BQ : 0;
   const int n_steps = (N - q_begin + C::BQ - 1) / C::BQ;  // >= 1 since k0 < N
 
+  // Block-sparse: the query steps (64 rows) whose 128-query block is live in this key tile's
+  // column of the block mask (the key tile is exactly one 128-key block), compacted into a list
+  // in LDS after the stages; steps past the list's end map past N.
+  int n_live = n_steps;
+  const uint16_t* live_list = nullptr;
+  if constexpr (SPARSE) {
+    static_assert(C::BKV == kSparseBlock && 2 * C::BQ == kSparseBlock, "tile / block mismatch");
+    uint16_t* list = smem + 2 * C::STAGE;
+    const uint8_t* mcol = a.sparse.mask +
+        (size_t)(a.sparse.mask_heads == 1 ? 0 : bh) * a.sparse.nb * a.sparse.nb + kt;
+    const int nb = a.sparse.nb;
+    n_live = build_live_list(list, reinterpret_cast<int*>(list + kSparseListMax), n_steps,
+                             [&](int t) {
+                               return mcol[(size_t)((q_begin + t * C::BQ) >> 7) * nb] != 0;
+                             });
+    live_list = list;
+  }
+  auto step_i0 = [&](int n) -> int {
+    if constexpr (SPARSE)
+      return n < n_live ? q_begin + (int)live_list[n] * C::BQ : q_begin + n_steps * C::BQ;
+    return q_begin + n * C::BQ;
+  };
+
   // Two register sets: tile i+2 is loading while tile i+1 (loaded one step earlier) is staged.
   u32x4 qreg[2][C::CHUNKS], oreg[2][C::CHUNKS];
   float lreg[2], dreg[2];
@@ -222,8 +246,9 @@ __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs 
       st16(os + row * C::ROW + cc * 8, oreg[set][u]);
     }
     if (wave == 0) {
-      // Rows beyond N get LSE = +inf, so that P = 0 there.
-      vec[lane] = (i0 + lane < N) ? lreg[set] * kLog2e : INFINITY;
+      // Rows beyond N, and rows that saw no key (LSE = -inf, block-sparse only), get +inf, so
+      // that P = 0 there.
+      vec[lane] = (i0 + lane < N && lreg[set] != -INFINITY) ? lreg[set] * kLog2e : INFINITY;
       vec[C::BQ + lane] = dreg[set];
     }
   };
@@ -349,20 +374,19 @@ __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs 
   // explicit wait, then start the second tile. All loads and LDS writes in the loop are
   // unconditional (tiles past N read zeros; their math is skipped), so the compiler counts
   // outstanding loads exactly and never waits on a prefetch before the math.
-  load_tile(0, q_begin);
-  store_tile(0, 0, q_begin);
+  load_tile(0, step_i0(0));
+  store_tile(0, 0, step_i0(0));
   wait_vmem_all();
-  load_tile(1, q_begin + C::BQ);
+  load_tile(1, step_i0(1));
   __syncthreads();
-  for (int step = 0; step < n_steps; step += 2) {
-    const int i0 = q_begin + step * C::BQ;
-    load_tile(0, i0 + 2 * C::BQ);
-    step_math(0, i0);
-    store_tile(1, 1, i0 + C::BQ);
+  for (int step = 0; step < n_live; step += 2) {
+    load_tile(0, step_i0(step + 2));
+    step_math(0, step_i0(step));
+    store_tile(1, 1, step_i0(step + 1));
     __syncthreads();
-    load_tile(1, i0 + 3 * C::BQ);
-    step_math(1, i0 + C::BQ);
-    store_tile(0, 0, i0 + 2 * C::BQ);
+    load_tile(1, step_i0(step + 3));
+    step_math(1, step_i0(step + 1));
+    store_tile(0, 0, step_i0(step + 2));
     __syncthreads();
   }
 
@@ -403,7 +427,7 @@ struct Dq {
   static constexpr int MIN_WG = (D == 64) ? 2 : 1;
 };
 
-template <int D, bool IS_BF16, bool G_F32, bool CAUSAL, bool DROP>
+template <int D, bool IS_BF16, bool G_F32, bool CAUSAL, bool DROP, bool SPARSE>
 __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
   using C = Dq<D>;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
@@ -453,6 +477,23 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
   const int kv_end = CAUSAL ? min(N, qt0 + C::BR) : N;
   const int n_kt = (kv_end + C::BC - 1) / C::BC;
 
+  // Block-sparse: live K/V tiles of this query tile's row of the block mask (as in the forward).
+  int n_live = n_kt;
+  const uint16_t* live_list = nullptr;
+  if constexpr (SPARSE) {
+    static_assert(C::BR == kSparseBlock && 2 * C::BC == kSparseBlock, "tile / block mismatch");
+    uint16_t* list = smem + 2 * C::STAGE;
+    const uint8_t* mrow = a.sparse.mask +
+        ((size_t)(a.sparse.mask_heads == 1 ? 0 : bh) * a.sparse.nb + tile) * a.sparse.nb;
+    n_live = build_live_list(list, reinterpret_cast<int*>(list + kSparseListMax), n_kt,
+                             [&](int t) { return mrow[t >> 1] != 0; });
+    live_list = list;
+  }
+  auto tile_j0 = [&](int n) -> int {
+    if constexpr (SPARSE) return n < n_live ? (int)live_list[n] * C::BC : n_kt * C::BC;
+    return n * C::BC;
+  };
+
   u32x4 kreg[2][C::CHUNKS], vreg[2][C::CHUNKS];
   auto load_tile = [&](int set, int j0) {
 #pragma unroll
@@ -477,11 +518,12 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
     }
   };
 
-  load_tile(0, 0);
+  load_tile(0, tile_j0(0));
   store_tile(0, 0);
   wait_vmem_all();
-  const float lse2 = qrow < N ? lse_raw * kLog2e : INFINITY;
-  load_tile(1, C::BC);
+  // Rows beyond N, and rows that saw no key (LSE = -inf, block-sparse only): P = 0.
+  const float lse2 = (qrow < N && lse_raw != -INFINITY) ? lse_raw * kLog2e : INFINITY;
+  load_tile(1, tile_j0(1));
   __syncthreads();
 
   auto tile_math = [&](int stage, int j0) {
@@ -564,13 +606,13 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
     }
   };
 
-  for (int jt = 0; jt < n_kt; jt += 2) {
-    load_tile(0, (jt + 2) * C::BC);
-    tile_math(0, jt * C::BC);
+  for (int jt = 0; jt < n_live; jt += 2) {
+    load_tile(0, tile_j0(jt + 2));
+    tile_math(0, tile_j0(jt));
     store_tile(1, 1);
     __syncthreads();
-    load_tile(1, (jt + 3) * C::BC);
-    tile_math(1, (jt + 1) * C::BC);
+    load_tile(1, tile_j0(jt + 3));
+    tile_math(1, tile_j0(jt + 1));
     store_tile(0, 0);
     __syncthreads();
   }
@@ -615,42 +657,54 @@ static hipError_t launch_dyn(K kern, int grid, int lds, BwdArgs a, hipStream_t s
   return hipGetLastError();
 }
 
-template <int D, bool IS_BF16, bool G_F32, bool CAUSAL, bool DROP>
+template <int D, bool IS_BF16, bool G_F32, bool CAUSAL, bool DROP, bool SPARSE>
 static hipError_t launch_grads(BwdArgs a, hipStream_t s, hipEvent_t ev_before,
                                hipEvent_t ev_after) {
   hipError_t e;
   if (ev_before && (e = hipEventRecord(ev_before, s)) != hipSuccess) return e;
   a.n_tiles = (a.N + Dkdv<D>::BKV - 1) / Dkdv<D>::BKV;
-  e = launch_dyn(bwd_dkdv_kernel<D, IS_BF16, G_F32, CAUSAL, DROP>, a.n_tiles * a.bh,
-                 Dkdv<D>::LDS_BYTES + (DROP ? Dkdv<D>::MASK_BYTES : 0), a, s);
+  e = launch_dyn(bwd_dkdv_kernel<D, IS_BF16, G_F32, CAUSAL, DROP, SPARSE>, a.n_tiles * a.bh,
+                 Dkdv<D>::LDS_BYTES + (DROP ? Dkdv<D>::MASK_BYTES : 0) +
+                     (SPARSE ? kSparseListBytes : 0),
+                 a, s);
   if (e != hipSuccess) return e;
   if (ev_after && (e = hipEventRecord(ev_after, s)) != hipSuccess) return e;
   a.n_tiles = (a.N + Dq<D>::BR - 1) / Dq<D>::BR;
-  return launch_dyn(bwd_dq_kernel<D, IS_BF16, G_F32, CAUSAL, DROP>, a.n_tiles * a.bh,
-                    Dq<D>::LDS_BYTES, a, s);
+  return launch_dyn(bwd_dq_kernel<D, IS_BF16, G_F32, CAUSAL, DROP, SPARSE>, a.n_tiles * a.bh,
+                    Dq<D>::LDS_BYTES + (SPARSE ? kSparseListBytes : 0), a, s);
 }
 
-template <int D, bool IS_BF16, bool G_F32, bool DROP>
+template <int D, bool IS_BF16, bool G_F32, bool DROP, bool SPARSE>
 static hipError_t launch_grads_c(const BwdArgs& a, bool causal, hipStream_t s,
                                  hipEvent_t ev_before, hipEvent_t ev_after) {
-  return causal ? launch_grads<D, IS_BF16, G_F32, true, DROP>(a, s, ev_before, ev_after)
-                : launch_grads<D, IS_BF16, G_F32, false, DROP>(a, s, ev_before, ev_after);
+  return causal ? launch_grads<D, IS_BF16, G_F32, true, DROP, SPARSE>(a, s, ev_before, ev_after)
+                : launch_grads<D, IS_BF16, G_F32, false, DROP, SPARSE>(a, s, ev_before, ev_after);
+}
+
+template <int D, bool IS_BF16, bool G_F32>
+static hipError_t launch_grads_m(const BwdArgs& a, bool causal, Mode mode, hipStream_t s,
+                                 hipEvent_t ev_before, hipEvent_t ev_after) {
+  switch (mode) {
+    case Mode::kDropout:
+      return launch_grads_c<D, IS_BF16, G_F32, true, false>(a, causal, s, ev_before, ev_after);
+    case Mode::kSparse:
+      return launch_grads_c<D, IS_BF16, G_F32, false, true>(a, causal, s, ev_before, ev_after);
+    default:
+      return launch_grads_c<D, IS_BF16, G_F32, false, false>(a, causal, s, ev_before, ev_after);
+  }
 }
 
 template <int D, bool IS_BF16>
-static hipError_t launch_all(const BwdArgs& a, bool o_f32, bool g_f32, bool causal, bool drop,
+static hipError_t launch_all(const BwdArgs& a, bool o_f32, bool g_f32, bool causal, Mode drop,
                              hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after) {
   hipError_t e = launch_pre<D, IS_BF16>(a, o_f32, s);
   if (e != hipSuccess) return e;
-  if (g_f32)
-    return drop ? launch_grads_c<D, IS_BF16, true, true>(a, causal, s, ev_before, ev_after)
-                : launch_grads_c<D, IS_BF16, true, false>(a, causal, s, ev_before, ev_after);
-  return drop ? launch_grads_c<D, IS_BF16, false, true>(a, causal, s, ev_before, ev_after)
-              : launch_grads_c<D, IS_BF16, false, false>(a, causal, s, ev_before, ev_after);
+  return g_f32 ? launch_grads_m<D, IS_BF16, true>(a, causal, drop, s, ev_before, ev_after)
+               : launch_grads_m<D, IS_BF16, false>(a, causal, drop, s, ev_before, ev_after);
 }
 
 hipError_t launch_backward(const BwdArgs& a, int d, int in_dtype, int o_dtype, int grad_dtype,
-                           bool causal, bool drop, hipStream_t s, hipEvent_t ev_before,
+                           bool causal, Mode drop, hipStream_t s, hipEvent_t ev_before,
                            hipEvent_t ev_after) {
   const bool bf = in_dtype == 2;
   const bool o_f32 = o_dtype == 0;

@@ -185,6 +185,36 @@ __device__ __forceinline__ uint32_t keep_bits8(const DropParams& dp, uint32_t gr
   return bits;
 }
 
+// Block-sparse attention: the mask has one byte per (128-query block, 128-key block); a kernel
+// visits only the tiles whose block is nonzero. Sequences with more than kSparseMaxN elements are
+// rejected by the C ABI, so a workgroup's list of live tiles (64 rows each) fits kSparseListMax
+// entries.
+constexpr int kSparseBlock = 128;
+constexpr int kSparseMaxN = 65536;
+constexpr int kSparseListMax = kSparseMaxN / 64;
+constexpr int kSparseListBytes = kSparseListMax * 2 + 16;  // the list, then its length
+
+// Compacts the indices t in [0, n) for which live(t) holds into list[0 .. count), in ascending
+// order, with wave 0 of the workgroup (one ballot per 64 candidates), and returns count to every
+// thread after a workgroup barrier. list and count_slot point into LDS.
+template <typename F>
+__device__ __forceinline__ int build_live_list(uint16_t* list, int* count_slot, int n, F live) {
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    int cnt = 0;
+    for (int base = 0; base < n; base += 64) {
+      const int t = base + tid;
+      const bool lv = (t < n) && live(t);
+      const unsigned long long bal = __ballot(lv);
+      if (lv) list[cnt + __popcll(bal & ((1ull << tid) - 1ull))] = (uint16_t)t;
+      cnt += __popcll(bal);
+    }
+    if (tid == 0) *count_slot = cnt;
+  }
+  __syncthreads();
+  return *count_slot;
+}
+
 // 16-byte global load / store helpers.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }

@@ -85,7 +85,7 @@ constexpr int fwd_qb() {
   return 1;
 }
 
-template <int D, bool IS_BF16, bool O_F32, bool CAUSAL, int QB, bool DROP>
+template <int D, bool IS_BF16, bool O_F32, bool CAUSAL, int QB, bool DROP, bool SPARSE>
 __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
   using C = Fwd16<D, IS_BF16, O_F32, CAUSAL, QB>;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
@@ -140,6 +140,25 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
 
   const int kv_end = CAUSAL ? min(N, qt0 + C::BR) : N;
   const int n_kt = (kv_end + C::BC - 1) / C::BC;
+
+  // Block-sparse: the K/V tiles this query tile visits are those whose 128-key block is live in
+  // its row of the block mask (the query tile is exactly one 128-row block). They are compacted
+  // into a list in LDS after the two stages; tiles past the list's end map past kv_end.
+  int n_live = n_kt;
+  const uint16_t* live_list = nullptr;
+  if constexpr (SPARSE) {
+    static_assert(C::BR == kSparseBlock && 2 * C::BC == kSparseBlock, "tile / block mismatch");
+    uint16_t* list = smem + 2 * C::STAGE;
+    const uint8_t* mrow = a.sparse.mask +
+        ((size_t)(a.sparse.mask_heads == 1 ? 0 : bh) * a.sparse.nb + tile) * a.sparse.nb;
+    n_live = build_live_list(list, reinterpret_cast<int*>(list + kSparseListMax), n_kt,
+                             [&](int t) { return mrow[t >> 1] != 0; });
+    live_list = list;
+  }
+  auto tile_j0 = [&](int n) -> int {
+    if constexpr (SPARSE) return n < n_live ? (int)live_list[n] * C::BC : n_kt * C::BC;
+    return n * C::BC;
+  };
 
   // Global -> register staging of one K/V tile (keys beyond N read as zeros). K rows go to LDS
   // in the permuted order of krow_of_key; V rows stay in key order (the P.V operand is read
@@ -294,22 +313,22 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
   // before the loop; tile 1 is then in flight when the loop starts. Every load and LDS write in
   // the loop is unconditional (tiles past the end read zeros and their math is skipped), so the
   // compiler counts outstanding loads exactly.
-  load_tile(0, 0);
+  load_tile(0, tile_j0(0));
   store_tile(0, 0);
   wait_vmem_all();
-  load_tile(1, C::BC);
+  load_tile(1, tile_j0(1));
   __syncthreads();
 
   // Iteration jt: start loading tile jt+2, do the math of tile jt, write tile jt+1 (loaded during
   // the previous iteration) into the other LDS stage, barrier. Unrolled by two so that register
   // sets and LDS stages are compile-time.
-  for (int jt = 0; jt < n_kt; jt += 2) {
-    load_tile(0, (jt + 2) * C::BC);
-    tile_math(0, jt * C::BC);
+  for (int jt = 0; jt < n_live; jt += 2) {
+    load_tile(0, tile_j0(jt + 2));
+    tile_math(0, tile_j0(jt));
     store_tile(1, 1);
     __syncthreads();
-    load_tile(1, (jt + 3) * C::BC);
-    tile_math(1, (jt + 1) * C::BC);
+    load_tile(1, tile_j0(jt + 3));
+    tile_math(1, tile_j0(jt + 1));
     store_tile(0, 0);
     __syncthreads();
   }
@@ -319,10 +338,13 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
   for (int qb = 0; qb < QB; ++qb) {
     const int qrow = qw0 + qb * 32 + r;
     const float l_tot = halves_sum(l_run[qb]);
-    // With dropout, kept probabilities are scaled by 1 / keep rate.
-    const float inv = (DROP ? a.drop.keep_scale : 1.f) / l_tot;
+    // With dropout, kept probabilities are scaled by 1 / keep rate. A row that saw no key at all
+    // (possible only with a block mask) has l = 0: its output is 0 and its LSE -inf.
+    const bool empty = SPARSE && l_tot == 0.f;
+    const float inv = empty ? 0.f : (DROP ? a.drop.keep_scale : 1.f) / l_tot;
     if (qrow < N) {
-      if (g == 0) a.lse[(size_t)bh * N + qrow] = (m_run[qb] + fast_log2(l_tot)) * kLn2;
+      if (g == 0)
+        a.lse[(size_t)bh * N + qrow] = empty ? -INFINITY : (m_run[qb] + fast_log2(l_tot)) * kLn2;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
@@ -482,27 +504,34 @@ __global__ __launch_bounds__(256, 2) void fwd32_kernel(FwdArgs a) {
 // ----------------------------------------------------------------------------------------
 // Host-side launchers (called by the C ABI after validation).
 // ----------------------------------------------------------------------------------------
-template <int D, bool IS_BF16, bool O_F32, bool CAUSAL, int QB, bool DROP>
+template <int D, bool IS_BF16, bool O_F32, bool CAUSAL, int QB, bool DROP, bool SPARSE>
 static hipError_t launch16(FwdArgs a, hipStream_t s) {
   using C = Fwd16<D, IS_BF16, O_F32, CAUSAL, QB>;
   a.n_tiles = (a.N + C::BR - 1) / C::BR;
   const int grid = a.n_tiles * a.bh;
-  auto kern = fwd16_kernel<D, IS_BF16, O_F32, CAUSAL, QB, DROP>;
+  constexpr int lds = C::LDS_BYTES + (SPARSE ? kSparseListBytes : 0);
+  auto kern = fwd16_kernel<D, IS_BF16, O_F32, CAUSAL, QB, DROP, SPARSE>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), C::LDS_BYTES, s, a);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), lds, s, a);
   return hipGetLastError();
 }
 
-template <int D, bool IS_BF16, bool O_F32>
-static hipError_t launch16_c(FwdArgs a, bool causal, bool drop, hipStream_t s) {
+template <int D, bool IS_BF16, bool O_F32, bool DROP, bool SPARSE>
+static hipError_t launch16_m(FwdArgs a, bool causal, hipStream_t s) {
   constexpr int QB = fwd_qb<D>();
-  if (drop)
-    return causal ? launch16<D, IS_BF16, O_F32, true, QB, true>(a, s)
-                  : launch16<D, IS_BF16, O_F32, false, QB, true>(a, s);
-  return causal ? launch16<D, IS_BF16, O_F32, true, QB, false>(a, s)
-                : launch16<D, IS_BF16, O_F32, false, QB, false>(a, s);
+  return causal ? launch16<D, IS_BF16, O_F32, true, QB, DROP, SPARSE>(a, s)
+                : launch16<D, IS_BF16, O_F32, false, QB, DROP, SPARSE>(a, s);
+}
+
+template <int D, bool IS_BF16, bool O_F32>
+static hipError_t launch16_c(FwdArgs a, bool causal, Mode mode, hipStream_t s) {
+  switch (mode) {
+    case Mode::kDropout: return launch16_m<D, IS_BF16, O_F32, true, false>(a, causal, s);
+    case Mode::kSparse: return launch16_m<D, IS_BF16, O_F32, false, true>(a, causal, s);
+    default: return launch16_m<D, IS_BF16, O_F32, false, false>(a, causal, s);
+  }
 }
 
 template <int D>
@@ -518,9 +547,9 @@ static hipError_t launch32(FwdArgs a, bool causal, hipStream_t s) {
 }
 
 hipError_t launch_forward(const FwdArgs& a, int d, int in_dtype, int o_f32, bool causal,
-                          bool drop, hipStream_t s) {
+                          Mode drop, hipStream_t s) {
   if (in_dtype == 0) {
-    if (drop) return hipErrorInvalidValue;  // rejected by the C ABI before this point
+    if (drop != Mode::kPlain) return hipErrorInvalidValue;  // rejected by the C ABI already
     return d == 64 ? launch32<64>(a, causal, s) : launch32<128>(a, causal, s);
   }
   const bool bf = in_dtype == 2;

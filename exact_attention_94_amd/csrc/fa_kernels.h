@@ -9,6 +9,14 @@
 
 namespace fa {
 
+// Block mask [mask_heads][nb][nb] (device memory, one byte per 128 x 128 block, nonzero = live),
+// nb = ceil(N / 128); mask_heads is 1 (shared by all heads) or B*H.
+struct SparseParams {
+  const uint8_t* mask;
+  int mask_heads;
+  int nb;
+};
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -20,6 +28,7 @@ struct FwdArgs {
   int n_tiles;  // query tiles per head (set by the launcher)
   float c;      // scale * log2(e), never 0
   DropParams drop;  // used only by the dropout instances
+  SparseParams sparse;  // used only by the block-sparse instances
 };
 
 struct BwdArgs {
@@ -47,15 +56,18 @@ struct BwdArgs {
   float scale;
   float c;  // scale * log2(e)
   DropParams drop;  // used only by the dropout instances
+  SparseParams sparse;  // used only by the block-sparse instances
 };
 
 // in_dtype / o_dtype / grad_dtype codes follow fa_dtype: 0 = f32, 1 = f16, 2 = bf16.
-// dropout: run the instances that apply the keep mask of a.drop (16-bit inputs only).
+// Variant of the kernels to run (16-bit inputs only for the last two).
+enum class Mode { kPlain = 0, kDropout = 1, kSparse = 2 };
+
 hipError_t launch_forward(const FwdArgs& a, int d, int in_dtype, int o_f32, bool causal,
-                          bool dropout, hipStream_t s);
+                          Mode mode, hipStream_t s);
 // ev_before / ev_after (may be null): recorded on `s` around the dK/dV kernel.
 hipError_t launch_backward(const BwdArgs& a, int d, int in_dtype, int o_dtype, int grad_dtype,
-                           bool causal, bool dropout, hipStream_t s, hipEvent_t ev_before,
+                           bool causal, Mode mode, hipStream_t s, hipEvent_t ev_before,
                            hipEvent_t ev_after);
 
 }  // namespace fa

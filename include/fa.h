@@ -136,6 +136,42 @@ fa_status fa_backward_dropout(const void* q, const void* k, const void* v, const
                               float dropout_p, uint64_t seed, uint32_t offset, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* Block size of the block-sparse masks: one mask byte covers 128 queries x 128 keys. */
+#define FA_SPARSE_BLOCK 128
+/* Longest sequence the block-sparse entry points accept. */
+#define FA_SPARSE_MAX_N 65536
+
+/*
+ * Block-sparse forward pass ("FlashAttention 为什么不需要存下注意力矩阵" §06: once attention is cut
+ * into blocks, whole blocks can be skipped; the causal case of §04 4.5 generalised to any
+ * pattern of blocks is block-sparse attention).
+ *
+ *   block_mask  device array of mask_heads x nb x nb bytes, nb = ceil(N / FA_SPARSE_BLOCK),
+ *               row-major: block_mask[(hm * nb + qb) * nb + kb] != 0 lets queries
+ *               128*qb .. 128*qb + 127 see keys 128*kb .. 128*kb + 127 (read only, caller-owned)
+ *   mask_heads  1 (one mask for every (b, h)) or B*H (mask of head b*H + h at index b*H + h)
+ * Query i sees key j iff its block is nonzero (and j <= i when causal). Blocks that are zero are
+ * never loaded or computed. A query that sees no key gets O = 0 and LSE = -inf. Other arguments
+ * as fa_forward; in_dtype must be FA_F16 or FA_BF16 and N <= FA_SPARSE_MAX_N
+ * (FA_ERR_UNSUPPORTED otherwise); a NULL mask or another mask_heads is FA_ERR_INVALID_ARG.
+ */
+fa_status fa_forward_blocksparse(const void* q, const void* k, const void* v, void* o,
+                                 float* lse, int B, int H, int N, int d, float scale, int causal,
+                                 fa_dtype in_dtype, fa_dtype o_dtype, const uint8_t* block_mask,
+                                 int mask_heads, void* stream);
+
+/*
+ * Backward pass of fa_forward_blocksparse with the same mask: invisible keys have P = 0 and only
+ * live blocks are visited; queries that saw no key (LSE = -inf) contribute nothing. Arguments,
+ * workspace and errors as fa_backward plus the mask arguments of fa_forward_blocksparse.
+ */
+fa_status fa_backward_blocksparse(const void* q, const void* k, const void* v, const void* o,
+                                  const void* dout, const float* lse, void* dq, void* dk,
+                                  void* dv, int B, int H, int N, int d, float scale, int causal,
+                                  fa_dtype in_dtype, fa_dtype o_dtype, fa_dtype grad_dtype,
+                                  const uint8_t* block_mask, int mask_heads, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /*
  * Profiling aid with no effect on results: after this call, every fa_backward call made by the
  * calling thread records `before` on its stream immediately before its dK/dV kernel (the

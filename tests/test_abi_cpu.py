@@ -145,6 +145,39 @@ def test_dropout_rejects_like_the_plain_calls():
     assert bwd_drop(causal=3) == B.FA_ERR_INVALID_ARG
 
 
+def fwd_sparse(mask=P, heads=1, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=3, N=300, d=64, scale=0.125, causal=0,
+             in_dtype=B.FA_F16, o_dtype=B.FA_F16)
+    a.update(kw)
+    return _lib().fa_forward_blocksparse(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"],
+                                         a["H"], a["N"], a["d"], a["scale"], a["causal"],
+                                         a["in_dtype"], a["o_dtype"], mask, heads, None)
+
+
+def bwd_sparse(mask=P, heads=1, **kw):
+    a = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=2, H=3, N=300, d=64,
+             scale=0.125, causal=0, in_dtype=B.FA_BF16, o_dtype=B.FA_F32, g_dtype=B.FA_F32,
+             ws=P, ws_bytes=1 << 30)
+    a.update(kw)
+    return _lib().fa_backward_blocksparse(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"],
+                                          a["dq"], a["dk"], a["dv"], a["B"], a["H"], a["N"],
+                                          a["d"], a["scale"], a["causal"], a["in_dtype"],
+                                          a["o_dtype"], a["g_dtype"], mask, heads, a["ws"],
+                                          a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("call", [fwd_sparse, bwd_sparse])
+def test_blocksparse_rejects(call):
+    assert call(mask=None) == B.FA_ERR_INVALID_ARG
+    assert call(heads=2) == B.FA_ERR_INVALID_ARG  # neither 1 nor B*H = 6
+    assert call(heads=0) == B.FA_ERR_INVALID_ARG
+    assert call(N=65537, B=1, H=1) == B.FA_ERR_UNSUPPORTED
+    assert call(in_dtype=B.FA_F32, o_dtype=B.FA_F32) == B.FA_ERR_UNSUPPORTED
+    assert call(d=96) == B.FA_ERR_UNSUPPORTED
+    assert call(N=0) == B.FA_ERR_INVALID_ARG
+    assert call(q=None, heads=6) == B.FA_ERR_INVALID_ARG
+
+
 def test_workspace_bytes():
     lib = _lib()
     ws = lib.fa_backward_workspace_bytes
