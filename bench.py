@@ -13,10 +13,12 @@ the forward (five products). The dK/dV kernel performs four products (S, dP, dV,
 the forward's FLOPs; the dQ kernel recomputes S and dP and forms dQ (three products), work the
 backward figure above does not count.
 
-The line also carries the same step with dropout p = 0.1 ("dropout": forward and backward times),
-which is not part of the headline value.
+The line also carries the same step with dropout p = 0.1 ("dropout") and with a block-sparse mask
+("blocksparse": forward and backward times and the rate over the visited blocks); neither is part
+of the headline value.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-dropout]
+                       [--no-blocksparse]
 """
 
 from __future__ import annotations
@@ -160,6 +162,62 @@ def time_dropout(fa, ev, stream, w, q, k, v, do, o, lse, grads, ws, steps, p=0.1
             "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2)}
 
 
+def local_global_mask(n_blocks):
+    """Sliding window of two 128-blocks (own and previous) plus global block 0 per query block."""
+    import numpy as np
+    m = np.zeros((n_blocks, n_blocks), dtype=np.uint8)
+    for qb in range(n_blocks):
+        m[qb, max(0, qb - 1):qb + 1] = 1
+        m[qb, 0] = 1
+    return m
+
+
+def time_blocksparse(fa, ev, stream, w, q, k, v, do, o, lse, grads, ws, steps):
+    """The same step with a block-sparse mask (local window + global block, 128 x 128 blocks, on
+    top of the causal rule). FLOPs count only the visited blocks (diagonal blocks at half, as the
+    causal convention does), so the rates compare with the dense figures."""
+    import numpy as np
+    import torch
+    nb = (w.N + 127) // 128
+    m = local_global_mask(nb)
+    live = np.tril(m)  # causal: blocks above the diagonal are never visited
+    diag = np.trace(live)
+    eff_blocks = float(live.sum() - diag) + 0.5 * diag
+    f_fwd = 4.0 * w.B * w.H * 128 * 128 * w.d * eff_blocks
+    f_bwd = 2.5 * f_fwd
+    mask_t = torch.from_numpy(m).to(q.device)
+
+    def fwd():
+        fa.forward(q, k, v, scale=w.scale, causal=True, out=o, lse=lse, block_mask=mask_t)
+
+    def bwd():
+        fa.backward(q, k, v, o, do, lse, scale=w.scale, causal=True, grad_dtype=torch.float32,
+                    workspace=ws, grads=grads, block_mask=mask_t)
+
+    for _ in range(2):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    e = [[ev.create() for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        ev.record(e[i][0], stream)
+        fwd()
+        ev.record(e[i][1], stream)
+        bwd()
+        ev.record(e[i][2], stream)
+    torch.cuda.synchronize()
+    fwd_ms = sum(ev.ms(x[0], x[1]) for x in e) / steps
+    bwd_ms = sum(ev.ms(x[1], x[2]) for x in e) / steps
+    for x in e:
+        for y in x:
+            ev.destroy(y)
+    return {"pattern": "window of 2 blocks + global block 0, 128x128 blocks, causal",
+            "live_block_fraction": round(float(live.sum()) / (nb * (nb + 1) / 2), 4),
+            "steps": steps, "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+            "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
+            "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,6 +227,8 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--no-dropout", action="store_true",
                     help="skip the extra timing of the dropout path (p = 0.1)")
+    ap.add_argument("--no-blocksparse", action="store_true",
+                    help="skip the extra timing of the block-sparse path")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -302,6 +362,9 @@ def main():
     if not args.no_dropout:
         out["dropout"] = time_dropout(fa, ev, stream, w, q, k, v, do, o, lse, grads, ws,
                                       steps=min(K, 10))
+    if not args.no_blocksparse:
+        out["blocksparse"] = time_blocksparse(fa, ev, stream, w, q, k, v, do, o, lse, grads, ws,
+                                              steps=min(K, 10))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, t, heads=args.cpu_heads)
     print(json.dumps(out), flush=True)
