@@ -26,6 +26,8 @@ attn_bwd_ref    naive backward: dV = P^T dO, dP = dO V^T, D = rowsum(dP*P),
 attn_tiled_ref  the blockwise online-softmax recurrence in the pages' V1 loop order (outer K/V
                 block, inner Q block), exposing the m / l / corr trajectory.
 attn_rows_ref   the forward for a chosen subset of query rows, one row at a time, O(N d) per row.
+attn_decode_ref Nq query rows (the last Nq positions) over Nk >= Nq keys: the decoding case.
+attn_split_merge_ref  the same via per-chunk partial results merged by their LSEs (split-KV).
 
 The forward and backward take an optional dropout keep mask (philox.py generates it from a seed
 and an offset with the Philox-4x32-10 counter-based generator) and an optional visibility mask
@@ -40,7 +42,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["attn_fwd_ref", "attn_bwd_ref", "attn_tiled_ref", "attn_rows_ref",
-           "block_mask_to_elements"]
+           "block_mask_to_elements", "attn_decode_ref", "attn_split_merge_ref"]
 
 
 def _heads(x):
@@ -302,3 +304,71 @@ def attn_rows_ref(q, k, v, scale, causal, rows):
         o[n] = (e @ v[:hi]) / den
         lse[n] = mx + np.log(den)
     return o, lse
+
+
+def attn_decode_ref(q, k, v, scale, causal):
+    """Attention of Nq query rows over Nk >= Nq keys (the decoding case, N_q << N_k).
+
+    q: [..., Nq, d]; k, v: [..., Nk, d]. Same definition as attn_fwd_ref ([FA-V1] §2.2 steps
+    1-3, [FA-why] §03 3.1) with the queries taken as the LAST Nq positions of the sequence: when
+    causal, query i (0-based among the Nq) sees keys j <= Nk - Nq + i, which is the top-left rule
+    of [FA-why] §03 3.2 when Nq = Nk. Returns (O [..., Nq, d], LSE [..., Nq]).
+    """
+    qh, lead = _heads(q)
+    kh, _ = _heads(k)
+    vh, _ = _heads(v)
+    G, nq, _ = qh.shape
+    nk = kh.shape[1]
+    if nq > nk:
+        raise ValueError("decoding needs Nq <= Nk")
+    o = np.empty((G, nq, vh.shape[-1]))
+    lse = np.empty((G, nq))
+    for g in range(G):
+        s = scale * (qh[g] @ kh[g].T)
+        if causal:
+            qi = np.arange(nq)[:, None] + (nk - nq)
+            s[np.arange(nk)[None, :] > qi] = -np.inf
+        p, m, l = _softmax_rows(s)
+        o[g] = p @ vh[g]
+        lse[g] = m + np.log(l)
+    return o.reshape(lead + (nq, vh.shape[-1])), lse.reshape(lead + (nq,))
+
+
+def attn_split_merge_ref(q, k, v, scale, causal, chunk):
+    """Split-KV decoding: attention over each chunk of `chunk` keys separately, then one merge.
+
+    Per chunk c the partial result is (O_c, LSE_c) = attention restricted to the chunk's keys
+    (a chunk that a query cannot see has LSE_c = -inf and weight 0). The merge is the rescale of
+    the online-softmax recurrence applied to whole chunks ([FA-why] §03 3.2: the result does not
+    depend on how the keys are blocked):  LSE = log sum_c exp(LSE_c),
+    O = sum_c exp(LSE_c - LSE) O_c. Flash-Decoding is named, without details, in
+    "FlashAttention V1 技术深度解析" (conclusion) and "Flash Attention：一个数学技巧把内存省 5 倍" §七.
+    q: [..., Nq, d], k, v: [..., Nk, d]. Returns (O, LSE) like attn_decode_ref.
+    """
+    qh, lead = _heads(q)
+    kh, _ = _heads(k)
+    vh, _ = _heads(v)
+    G, nq, _ = qh.shape
+    nk = kh.shape[1]
+    starts = list(range(0, nk, chunk))
+    o = np.zeros((G, nq, vh.shape[-1]))
+    lse = np.empty((G, nq))
+    for g in range(G):
+        parts = []
+        for j0 in starts:
+            j1 = min(j0 + chunk, nk)
+            s = scale * (qh[g] @ kh[g][j0:j1].T)
+            if causal:
+                qi = np.arange(nq)[:, None] + (nk - nq)
+                s[np.arange(j0, j1)[None, :] > qi] = -np.inf
+            p, m, l = _softmax_rows(s)
+            with np.errstate(divide="ignore"):
+                parts.append((p @ vh[g][j0:j1], m + np.log(l)))
+        lses = np.stack([pl for _, pl in parts])           # [C, nq]
+        top = lses.max(axis=0)
+        w = np.exp(lses - top[None, :])                    # exp(-inf) = 0 for empty chunks
+        tot = w.sum(axis=0)
+        lse[g] = top + np.log(tot)
+        for (po, _), wc in zip(parts, w):
+            o[g] += (wc / tot)[:, None] * po
+    return o.reshape(lead + (nq, vh.shape[-1])), lse.reshape(lead + (nq,))
