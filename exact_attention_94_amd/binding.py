@@ -20,7 +20,8 @@ FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 # Every symbol include/fa.h declares.
 EXPORTS = ("fa_forward", "fa_forward_dropout", "fa_forward_blocksparse", "fa_backward",
            "fa_backward_dropout", "fa_backward_blocksparse", "fa_backward_workspace_bytes",
-           "fa_profile_backward_main", "fa_status_string")
+           "fa_decode_workspace_bytes", "fa_decode_forward", "fa_profile_backward_main",
+           "fa_status_string")
 
 SPARSE_BLOCK = 128  # queries x keys covered by one block-mask byte (FA_SPARSE_BLOCK)
 
@@ -63,6 +64,10 @@ def load(path=LIB_PATH):
     lib.fa_backward_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i,
                                             i, i, i, vp, i, vp, sz, vp]
     lib.fa_backward_blocksparse.restype = i
+    lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa_decode_workspace_bytes.restype = sz
+    lib.fa_decode_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
+    lib.fa_decode_forward.restype = i
     lib.fa_profile_backward_main.argtypes = [vp, vp]
     lib.fa_profile_backward_main.restype = i
     lib.fa_status_string.argtypes = [i]
@@ -221,3 +226,43 @@ def backward(q, k, v, o, dout, lse, scale=None, causal=False, grad_dtype=None, w
     if st != FA_OK:
         raise FAError(st, where)
     return dq, dk, dv
+
+
+def decode_workspace_bytes(B, H, Nq, Nk, d):
+    return int(load().fa_decode_workspace_bytes(B, H, Nq, Nk, d))
+
+
+def decode(q, k, v, scale=None, causal=False, o_dtype=None, out=None, lse=None, workspace=None):
+    """fa_decode_forward: q [B, H, Nq, d] (Nq <= 4) against k, v [B, H, Nk, d]. Returns (O, LSE).
+
+    The queries are the last Nq positions of the sequence (causal: query i sees keys
+    0 .. Nk - Nq + i). `workspace` (a uint8 GPU tensor) is allocated when not given.
+    """
+    torch = _torch()
+    _check_bhnd("q", q)
+    _check_bhnd("k", k)
+    _check_bhnd("v", v, k.shape)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if tuple(k.shape[:2]) != (B, H) or k.shape[3] != d:
+        raise ValueError(f"k has shape {tuple(k.shape)}, expected [{B}, {H}, Nk, {d}]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share a dtype")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o_dtype = q.dtype if o_dtype is None else o_dtype
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=o_dtype, device=q.device)
+    else:
+        _check_bhnd("out", out, q.shape)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(B, H, Nq, Nk, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = load().fa_decode_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  lse.data_ptr(), B, H, Nq, Nk, d, scale, int(bool(causal)),
+                                  dtype_code(q.dtype), dtype_code(out.dtype),
+                                  workspace.data_ptr(), workspace.numel(), _stream(q))
+    if st != FA_OK:
+        raise FAError(st, "fa_decode_forward")
+    return out, lse

@@ -284,6 +284,78 @@ fa_status fa_backward_blocksparse(const void* q, const void* k, const void* v, c
                        o_dtype, grad_dtype, nullptr, &sp, workspace, workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Decoding workspace: per (head, chunk, query slot) the unnormalised O (d floats), then the
+// (m, l) pairs, each section 256-byte aligned.
+struct DecLayout {
+  int n_split, chunk, slots;
+  size_t ml_off, total;
+};
+
+fa_status decode_layout(int B, int H, int Nq, int Nk, int d, DecLayout& L) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_INVALID_ARG;
+  if ((long long)B * H * Nk * d > 0x7FFFFFFFLL) return FA_ERR_INVALID_ARG;
+  if ((long long)Nk * d > (1LL << 30)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (Nq > 4) return FA_ERR_UNSUPPORTED;
+  if (Nq > Nk) return FA_ERR_INVALID_ARG;
+  const int bh = B * H;
+  fa::decode_plan(bh, Nk, d, L.n_split, L.chunk);
+  L.slots = Nq == 1 ? 1 : 4;
+  const size_t parts = (size_t)bh * L.n_split * L.slots;
+  L.ml_off = round_up(parts * d * sizeof(float), 256);
+  L.total = L.ml_off + round_up(parts * 2 * sizeof(float), 256);
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
+  DecLayout L;
+  return decode_layout(B, H, Nq, Nk, d, L) == FA_OK ? L.total : 0;
+}
+
+fa_status fa_decode_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                            fa_dtype in_dtype, fa_dtype o_dtype, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_INVALID_ARG;
+  if (!valid_dtype(in_dtype) || !valid_dtype(o_dtype)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+  DecLayout L;
+  const fa_status st = decode_layout(B, H, Nq, Nk, d, L);
+  if (st != FA_OK) return st;
+  if (in_dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (o_dtype != in_dtype && o_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if (!workspace || !aligned16(workspace) || workspace_bytes < L.total) return FA_ERR_WORKSPACE;
+
+  fa::DecArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.ml_off);
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.bh = B * H;
+  a.n_split = L.n_split;
+  a.chunk = L.chunk;
+  a.c = log2_scale(scale);
+  const hipError_t e = fa::launch_decode(a, d, (int)in_dtype, o_dtype == FA_F32, causal != 0,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 fa_status fa_profile_backward_main(void* before, void* after) {
   if ((before == nullptr) != (after == nullptr)) return FA_ERR_INVALID_ARG;
   t_prof_before = static_cast<hipEvent_t>(before);

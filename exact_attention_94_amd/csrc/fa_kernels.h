@@ -59,6 +59,24 @@ struct BwdArgs {
   SparseParams sparse;  // used only by the block-sparse instances
 };
 
+// Split-KV decoding: Nq (<= 4) query rows per head against Nk keys; partials per (head, chunk).
+struct DecArgs {
+  const void* q;  // [B,H,Nq,d]
+  const void* k;  // [B,H,Nk,d]
+  const void* v;
+  void* o;        // [B,H,Nq,d]
+  float* lse;     // [B,H,Nq]
+  float* part_o;  // [bh][n_split][nq_slots][d], nq_slots = 1 if Nq == 1 else 4
+  float* part_ml; // [bh][n_split][nq_slots][2]: running max (log2 domain) and sum
+  int Nq, Nk, bh, n_split, chunk;
+  float c;        // scale * log2(e)
+};
+
+// Chunking of Nk keys for bh heads (shared by the workspace size query and the launch).
+void decode_plan(int bh, int nk, int d, int& n_split, int& chunk);
+hipError_t launch_decode(const DecArgs& a, int d, int in_dtype, bool o_f32, bool causal,
+                         hipStream_t s);
+
 // in_dtype / o_dtype / grad_dtype codes follow fa_dtype: 0 = f32, 1 = f16, 2 = bf16.
 // Variant of the kernels to run (16-bit inputs only for the last two).
 enum class Mode { kPlain = 0, kDropout = 1, kSparse = 2 };

@@ -173,6 +173,35 @@ fa_status fa_backward_blocksparse(const void* q, const void* k, const void* v, c
                                   size_t workspace_bytes, void* stream);
 
 /*
+ * Bytes of device workspace fa_decode_forward needs for these sizes: per (head, key chunk, query)
+ * an fp32 partial output of d elements and its running maximum and sum. Returns 0 for sizes
+ * fa_decode_forward would reject.
+ */
+size_t fa_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d);
+
+/*
+ * Split-KV decoding forward: Nq query rows per head, the LAST Nq positions of a sequence of Nk
+ * keys (Flash-Decoding, named in "FlashAttention V1 技术深度解析" (conclusion) and
+ * "Flash Attention：一个数学技巧把内存省 5 倍" §七; the merge is the rescale of
+ * "FlashAttention 为什么不需要存下注意力矩阵" §03 3.2 applied to whole chunks of keys).
+ *
+ *   q        [B,H,Nq,d] in in_dtype (FA_F16 or FA_BF16), 1 <= Nq <= 4 and Nq <= Nk
+ *   k, v     [B,H,Nk,d] in in_dtype (e.g. a KV cache)
+ *   o        [B,H,Nq,d] in o_dtype (in_dtype or FA_F32), written
+ *   lse      [B,H,Nq] float32, written (natural-log logsumexp of the scaled scores)
+ *   causal   1: query i (0-based among the Nq) sees keys 0 .. Nk - Nq + i; 0: all Nk keys
+ *   workspace  device buffer of at least fa_decode_workspace_bytes(B, H, Nq, Nk, d) bytes,
+ *            16-byte aligned; contents ignored and clobbered
+ * Two kernels run on the stream: one workgroup per (head, chunk of keys) writes a partial result,
+ * then one workgroup per (head, query) merges the partials. Deterministic (no atomics).
+ * Errors as fa_forward; Nq > 4 returns FA_ERR_UNSUPPORTED, Nq > Nk FA_ERR_INVALID_ARG.
+ */
+fa_status fa_decode_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                            fa_dtype in_dtype, fa_dtype o_dtype, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * Profiling aid with no effect on results: after this call, every fa_backward call made by the
  * calling thread records `before` on its stream immediately before its dK/dV kernel (the
  * longest of its kernels) is launched and `after` immediately after it, so the caller can time

@@ -178,6 +178,51 @@ def test_blocksparse_rejects(call):
     assert call(q=None, heads=6) == B.FA_ERR_INVALID_ARG
 
 
+def dec(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=3, Nq=1, Nk=1000, d=128, scale=0.1, causal=0,
+             in_dtype=B.FA_BF16, o_dtype=B.FA_BF16, ws=P, ws_bytes=1 << 30)
+    a.update(kw)
+    return _lib().fa_decode_forward(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                                    a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"],
+                                    a["in_dtype"], a["o_dtype"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), B.FA_ERR_INVALID_ARG),
+    (dict(k=P + 8), B.FA_ERR_INVALID_ARG),
+    (dict(Nq=0), B.FA_ERR_INVALID_ARG),
+    (dict(Nk=0), B.FA_ERR_INVALID_ARG),
+    (dict(Nq=4, Nk=3), B.FA_ERR_INVALID_ARG),
+    (dict(Nq=5), B.FA_ERR_UNSUPPORTED),
+    (dict(d=96), B.FA_ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), B.FA_ERR_INVALID_ARG),
+    (dict(causal=2), B.FA_ERR_INVALID_ARG),
+    (dict(in_dtype=B.FA_F32, o_dtype=B.FA_F32), B.FA_ERR_UNSUPPORTED),
+    (dict(o_dtype=B.FA_F16), B.FA_ERR_UNSUPPORTED),
+    (dict(ws=None), B.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=100), B.FA_ERR_WORKSPACE),
+    (dict(B=1, H=1, Nk=(1 << 23) + 1), B.FA_ERR_INVALID_ARG),
+])
+def test_decode_rejects(kw, status):
+    assert dec(**kw) == status
+
+
+def test_decode_workspace_bytes():
+    lib = _lib()
+    ws = lib.fa_decode_workspace_bytes
+    # 6 heads, Nk = 1000: the plan asks for ceil(2048 / 6) = 342 chunks but at least 256 keys
+    # each -> 4 chunks; chunk = 250 rounded up to 256 -> ceil(1000 / 256) = 4 chunks.
+    # Nq = 1: one slot; O partials 6*4*1*128 floats, then 6*4*1*2 floats, 256-byte sections.
+    assert ws(2, 3, 1, 1000, 128) == 12288 + 256
+    # Nq = 2..4 use four query slots.
+    assert ws(2, 3, 3, 1000, 128) == 4 * 12288 + 768
+    assert ws(2, 3, 5, 1000, 128) == 0
+    assert ws(2, 3, 1, 1000, 96) == 0
+    assert ws(2, 3, 2, 1, 64) == 0
+    need = ws(2, 3, 1, 1000, 128)
+    assert dec(ws_bytes=need - 1) == B.FA_ERR_WORKSPACE
+
+
 def test_workspace_bytes():
     lib = _lib()
     ws = lib.fa_backward_workspace_bytes
