@@ -13,12 +13,13 @@ the forward (five products). The dK/dV kernel performs four products (S, dP, dV,
 the forward's FLOPs; the dQ kernel recomputes S and dP and forms dQ (three products), work the
 backward figure above does not count.
 
-The line also carries the same step with dropout p = 0.1 ("dropout") and with a block-sparse mask
-("blocksparse": forward and backward times and the rate over the visited blocks); neither is part
-of the headline value.
+The line also carries the same step with dropout p = 0.1 ("dropout"), with a block-sparse mask
+("blocksparse": forward and backward times and the rate over the visited blocks), and split-KV
+decoding of a long bf16 K/V cache ("decode": HBM bytes per second against the 8 TB/s peak); none
+of them is part of the headline value.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-dropout]
-                       [--no-blocksparse]
+                       [--no-blocksparse] [--no-decode]
 """
 
 from __future__ import annotations
@@ -218,6 +219,38 @@ def time_blocksparse(fa, ev, stream, w, q, k, v, do, o, lse, grads, ws, steps):
             "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2)}
 
 
+def time_decode(fa, ev, stream, dev, steps, B=4, H=32, nk=16384, d=128):
+    """Split-KV decoding of one query row per sequence against a bf16 K/V cache of nk keys:
+    HBM-bound, so the rate is bytes moved (K, V, Q read once, O and LSE written) per second
+    against the 8 TB/s HBM peak. The cache (537 MB here) exceeds the 256 MB last-level cache."""
+    import torch
+    g = torch.Generator(device=dev)
+    g.manual_seed(nk)
+    k = torch.randn((B, H, nk, d), device=dev, generator=g).to(torch.bfloat16)
+    v = torch.randn((B, H, nk, d), device=dev, generator=g).to(torch.bfloat16)
+    q = torch.randn((B, H, 1, d), device=dev, generator=g).to(torch.bfloat16)
+    out = torch.empty((B, H, 1, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, 1), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.decode_workspace_bytes(B, H, 1, nk, d), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        fa.decode(q, k, v, causal=True, out=out, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = ev.create(), ev.create()
+    ev.record(e0, stream)
+    for _ in range(steps):
+        fa.decode(q, k, v, causal=True, out=out, lse=lse, workspace=ws)
+    ev.record(e1, stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(e0, e1) / steps
+    ev.destroy(e0)
+    ev.destroy(e1)
+    nbytes = 2 * B * H * nk * d * 2 + B * H * d * 2 * 2 + B * H * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"B={B} H={H} Nq=1 Nk={nk} d={d} bf16 causal", "steps": steps,
+            "ms": round(ms, 4), "bytes": nbytes, "achieved_GBs": round(gbs, 1),
+            "hbm_peak_GBs": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -229,6 +262,8 @@ def main():
                     help="skip the extra timing of the dropout path (p = 0.1)")
     ap.add_argument("--no-blocksparse", action="store_true",
                     help="skip the extra timing of the block-sparse path")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the extra timing of split-KV decoding")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -365,6 +400,8 @@ def main():
     if not args.no_blocksparse:
         out["blocksparse"] = time_blocksparse(fa, ev, stream, w, q, k, v, do, o, lse, grads, ws,
                                               steps=min(K, 10))
+    if not args.no_decode:
+        out["decode"] = time_decode(fa, ev, stream, dev, steps=min(K, 20))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, t, heads=args.cpu_heads)
     print(json.dumps(out), flush=True)
