@@ -11,20 +11,24 @@
 // With one query row per head there is no matrix product worth a matrix core (an MFMA would use
 // 1 of its 32 columns): every K and V byte is read once and used once, so the split kernel is
 // HBM-bound and is built for bandwidth. A key row (d = 128 bf16: 256 bytes) is loaded by 16
-// lanes with 16-byte buffer loads, four loads per lane and tensor in flight; the partial dot
+// lanes with 16-byte buffer loads, up to eight loads per lane and tensor in flight; the partial dot
 // products are summed across those lanes, and each lane keeps the running (m, l) and 8 output
 // elements of its stream of keys. Streams are merged inside the wave by lane exchanges, then
-// across the workgroup's waves through LDS.
+// across the workgroup's waves through LDS. K and V are read with the non-temporal (streaming)
+// cache policy: each byte is used once, so keeping it in the caches only evicts other data
+// (measured: 5.7 -> 6.5 TB/s on a 1 GB bf16 cache).
 #include "fa_device.h"
 #include "fa_kernels.h"
 
 namespace fa {
 
-template <int D>
+template <int D, int NQ>
 struct Dec {
   static constexpr int LPK = D / 8;        // lanes per key row (8 elements = 16 bytes each)
   static constexpr int KPW = 64 / LPK;     // key rows per wave and load instruction
-  static constexpr int U = 4;              // loads in flight per lane and tensor
+  // Loads in flight per lane and tensor: 8 for one query row; 4 for four rows, whose
+  // accumulators leave fewer registers.
+  static constexpr int U = NQ == 1 ? 8 : 4;
   static constexpr int NW = 4;             // waves per workgroup
   static constexpr int KPI = KPW * U * NW; // keys per workgroup iteration
 };
@@ -33,7 +37,7 @@ struct Dec {
 // running maximum m (log2 domain, sentinel -3e38 when nothing was visible) and its sum l.
 template <int D, int NQ, bool IS_BF16, bool CAUSAL>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
-  using C = Dec<D>;
+  using C = Dec<D, NQ>;
   __shared__ float red[C::NW][NQ][C::LPK][10];
 
   const int lane = threadIdx.x & 63;
@@ -80,8 +84,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
     for (int u = 0; u < C::U; ++u) {
       key[u] = j0 + (u * C::NW + wave) * C::KPW + sub;
       const uint32_t off = (uint32_t)(key[u] * D + dc * 8) * 2;  // past Nk: zeros
-      kr[u] = buf_ld16(krs, off);
-      vr[u] = buf_ld16(vrs, off);
+      kr[u] = buf_ld16_stream(krs, off);
+      vr[u] = buf_ld16_stream(vrs, off);
     }
     float kf[C::U][8], vf[C::U][8];
 #pragma unroll
@@ -183,23 +187,68 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecArgs a) {
   }
 }
 
-// One workgroup of D threads per (head, query): thread t merges element t of O over the chunks.
+// Block-wide reduction of one float per thread (256 threads) through LDS.
+template <bool MAX>
+__device__ __forceinline__ float block_reduce(float x, float* scratch) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float y = __shfl_xor(x, off);
+    x = MAX ? __builtin_fmaxf(x, y) : x + y;
+  }
+  const int t = threadIdx.x;
+  if ((t & 63) == 0) scratch[t >> 6] = x;
+  __syncthreads();
+  x = scratch[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) x = MAX ? __builtin_fmaxf(x, scratch[w]) : x + scratch[w];
+  __syncthreads();
+  return x;
+}
+
+// One workgroup of 256 threads per (head, query). The chunks' maxima and weights
+// w_c = 2^(m_c - M) are computed once per chunk (threads over chunks); then thread t accumulates
+// element t % D of O over the chunks c = t / D (mod 256 / D), with several loads in flight, and
+// the 256 / D partial sums are added through LDS. The number of chunks never exceeds
+// kDecodeMaxSplit, so their weights fit in LDS.
 template <int D, int NQ, bool IS_BF16, bool O_F32>
-__global__ __launch_bounds__(128) void decode_merge_kernel(DecArgs a) {
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecArgs a) {
+  __shared__ float wts[kDecodeMaxSplit];
+  __shared__ float scratch[4];
+  __shared__ float osum[256];
+  constexpr int G = 256 / D;  // chunk groups
   const int t = threadIdx.x;
   const int qi = blockIdx.x % a.Nq;
   const int bh = blockIdx.x / a.Nq;
-  const size_t base = (size_t)bh * a.n_split;
+  const int ns = a.n_split;
+  const size_t base = (size_t)bh * ns;
   float mx = -3.0e38f;
-  for (int s = 0; s < a.n_split; ++s) mx = __builtin_fmaxf(mx, a.part_ml[((base + s) * NQ + qi) * 2]);
-  float lsum = 0.f, acc = 0.f;
-  for (int s = 0; s < a.n_split; ++s) {
-    const size_t p = (base + s) * NQ + qi;
+  for (int c = t; c < ns; c += 256) mx = __builtin_fmaxf(mx, a.part_ml[((base + c) * NQ + qi) * 2]);
+  mx = block_reduce<true>(mx, scratch);
+  float ls = 0.f;
+  for (int c = t; c < ns; c += 256) {
+    const size_t p = (base + c) * NQ + qi;
     const float w = fast_exp2(a.part_ml[p * 2] - mx);
-    lsum = __builtin_fmaf(a.part_ml[p * 2 + 1], w, lsum);
-    acc = __builtin_fmaf(a.part_o[p * D + t], w, acc);
+    wts[c] = w;
+    ls = __builtin_fmaf(a.part_ml[p * 2 + 1], w, ls);
   }
-  const float out = acc / lsum;
+  const float lsum = block_reduce<false>(ls, scratch);  // its barrier also publishes wts
+  const int dd = t % D, grp = t / D;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  int c = grp;
+  for (; c + 3 * G < ns; c += 4 * G) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      acc[u] = __builtin_fmaf(a.part_o[((base + c + u * G) * NQ + qi) * D + dd], wts[c + u * G],
+                              acc[u]);
+  }
+  for (; c < ns; c += G) acc[0] = __builtin_fmaf(a.part_o[((base + c) * NQ + qi) * D + dd], wts[c], acc[0]);
+  osum[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  __syncthreads();
+  if (t >= D) return;
+  float tot = osum[t];
+#pragma unroll
+  for (int g2 = 1; g2 < G; ++g2) tot += osum[t + g2 * D];
+  const float out = tot / lsum;
   const size_t oi = ((size_t)bh * a.Nq + qi) * D + t;
   if constexpr (O_F32) {
     static_cast<float*>(a.o)[oi] = out;
@@ -217,14 +266,14 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(DecArgs a) {
 void decode_plan(int bh, int nk, int d, int& n_split, int& chunk) {
   (void)d;
   // Enough workgroups to keep every CU streaming (about 8 per CU), chunks of at least 256 keys
-  // and a multiple of 128 (a whole number of workgroup iterations for both head dims).
-  const int target = 2048;
+  // and a multiple of 256 (a whole number of workgroup iterations for every instance).
+  const int target = kDecodeMaxSplit;
   int want = (target + bh - 1) / bh;
   const int max_split = (nk + 255) / 256;
   if (want > max_split) want = max_split;
   if (want < 1) want = 1;
   chunk = (nk + want - 1) / want;
-  chunk = (chunk + 127) / 128 * 128;
+  chunk = (chunk + 255) / 256 * 256;
   n_split = (nk + chunk - 1) / chunk;
 }
 
@@ -239,9 +288,9 @@ static hipError_t launch_dec(const DecArgs& a, bool causal, bool o_f32, hipStrea
   if (e != hipSuccess) return e;
   const int mgrid = a.bh * a.Nq;
   if (o_f32)
-    hipLaunchKernelGGL((decode_merge_kernel<D, NQ, IS_BF16, true>), dim3(mgrid), dim3(D), 0, s, a);
+    hipLaunchKernelGGL((decode_merge_kernel<D, NQ, IS_BF16, true>), dim3(mgrid), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_merge_kernel<D, NQ, IS_BF16, false>), dim3(mgrid), dim3(D), 0, s, a);
+    hipLaunchKernelGGL((decode_merge_kernel<D, NQ, IS_BF16, false>), dim3(mgrid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

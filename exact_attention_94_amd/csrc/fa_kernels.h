@@ -72,6 +72,9 @@ struct DecArgs {
   float c;        // scale * log2(e)
 };
 
+// Upper bound of the number of key chunks per head (the merge kernel keeps their weights in LDS).
+constexpr int kDecodeMaxSplit = 2048;
+
 // Chunking of Nk keys for bh heads (shared by the workspace size query and the launch).
 void decode_plan(int bh, int nk, int d, int& n_split, int& chunk);
 hipError_t launch_decode(const DecArgs& a, int d, int in_dtype, bool o_f32, bool causal,
