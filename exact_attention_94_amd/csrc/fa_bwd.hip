@@ -97,6 +97,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, long long rows)
 __device__ __forceinline__ int perm_row(int e) {
   return 8 * (2 * (e >> 4) + ((e >> 2) & 1)) + 4 * ((e >> 3) & 1) + (e & 3);
 }
+// Inverse of perm_row: the element placed on LDS row R.
+__device__ __forceinline__ int row_key(int R) {
+  return 16 * (R >> 4) + 8 * ((R >> 2) & 1) + 4 * ((R >> 3) & 1) + (R & 3);
+}
 
 // Workgroup -> (head, tile). With B*H a multiple of 8, each XCD (blockIdx % 8) works on its own
 // heads so that one head's tiles share an L2. `reverse` dispatches the highest tile first.
@@ -136,11 +140,11 @@ struct Dkdv {
   static constexpr int QBS = BQ / 32;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int ROW = D + kLdsPad;     // Q / dO tile row stride (elements)
-  static constexpr int TILE = BQ * ROW;
+  static constexpr int NW = 4;
+  static constexpr int TILE = BQ * D;  // Q / dO tiles: swizzled rows, no padding
   static constexpr int STAGE = 2 * TILE + 2 * BQ * 2;  // Q, dO, then LSE*log2e and D (fp32)
   static constexpr int LDS_BYTES = 2 * STAGE * 2;
-  static constexpr int CHUNKS = BQ * D / 8 / NT;  // 16-byte chunks per thread per tile
+  static constexpr int LD_INSTR = BQ * D * 2 / 1024;  // 1 KB direct loads per tile and tensor
   static constexpr int MIN_WG = (D == 64) ? 2 : 1;
   // Dropout instances: one 32-bit keep word per (wave, query of the step) after the stages.
   static constexpr int MASK_BYTES = 4 * BQ * 4;
@@ -220,36 +224,41 @@ __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs 
     return q_begin + n * C::BQ;
   };
 
-  // Two register sets: tile i+2 is loading while tile i+1 (loaded one step earlier) is staged.
-  u32x4 qreg[2][C::CHUNKS], oreg[2][C::CHUNKS];
-  float lreg[2], dreg[2];
-  auto load_tile = [&](int set, int i0) {
+  // Q and dO tiles by direct buffer->LDS loads into swizzled rows (swz_off), rows in perm_row
+  // order (LDS row R holds query row_key(R) of the step): lane l of 1 KB load t deposits 16 bytes
+  // at element 512 t + 8 l of the tile. The step's LSE and D go through registers, since they
+  // are transformed on the way (LSE * log2 e, +inf for rows that must give P = 0).
+  constexpr int LPW = C::LD_INSTR / C::NW;  // loads per wave and tensor
+  uint32_t toff[LPW];
 #pragma unroll
-    for (int u = 0; u < C::CHUNKS; ++u) {
-      const uint32_t off = (uint32_t)(i0 * D + (tid + u * C::NT) * 8) * 2;
-      qreg[set][u] = buf_ld16(qrs, off);
-      oreg[set][u] = buf_ld16(dors, off);
-    }
-    lreg[set] = buf_ldf(lrs, (uint32_t)(i0 + lane) * 4);
-    dreg[set] = buf_ldf(drs, (uint32_t)(i0 + lane) * 4);
-  };
-  auto store_tile = [&](int set, int stage, int i0) {
+  for (int i = 0; i < LPW; ++i) {
+    const int e = (wave + i * C::NW) * 512 + lane * 8;
+    const int R = e / D;
+    const int cch = ((e % D) >> 3) ^ swz(R);
+    toff[i] = (uint32_t)(((R & ~31) + row_key(R & 31)) * D + cch * 8) * 2;
+  }
+  float lreg, dreg;
+  auto issue_tile = [&](int stage, int i0) {
     uint16_t* qs = smem + stage * C::STAGE;
     uint16_t* os = qs + C::TILE;
-    float* vec = reinterpret_cast<float*>(qs + 2 * C::TILE);
+    const uint32_t base = (uint32_t)i0 * D * 2;
 #pragma unroll
-    for (int u = 0; u < C::CHUNKS; ++u) {
-      const int chunk = tid + u * C::NT;
-      const int qq = chunk / (D / 8), cc = chunk % (D / 8);
-      const int row = (qq & ~31) + perm_row(qq & 31);
-      st16(qs + row * C::ROW + cc * 8, qreg[set][u]);
-      st16(os + row * C::ROW + cc * 8, oreg[set][u]);
+    for (int i = 0; i < LPW; ++i) {
+      const int t = wave + i * C::NW;
+      buf_ld16_lds(qrs, base + toff[i], qs + t * 512);
+      buf_ld16_lds(dors, base + toff[i], os + t * 512);
     }
+    lreg = buf_ldf(lrs, (uint32_t)(i0 + lane) * 4);
+    dreg = buf_ldf(drs, (uint32_t)(i0 + lane) * 4);
+  };
+  // After the loads of issue_tile have completed: the row vectors of the step.
+  auto store_vec = [&](int stage, int i0) {
+    float* vec = reinterpret_cast<float*>(smem + stage * C::STAGE + 2 * C::TILE);
     if (wave == 0) {
       // Rows beyond N, and rows that saw no key (LSE = -inf, block-sparse only), get +inf, so
       // that P = 0 there.
-      vec[lane] = (i0 + lane < N && lreg[set] != -INFINITY) ? lreg[set] * kLog2e : INFINITY;
-      vec[C::BQ + lane] = dreg[set];
+      vec[lane] = (i0 + lane < N && lreg != -INFINITY) ? lreg * kLog2e : INFINITY;
+      vec[C::BQ + lane] = dreg;
     }
   };
 
@@ -276,8 +285,8 @@ __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs 
 #pragma unroll
       for (int qb = 0; qb < C::QBS; ++qb) {
         Frag16 qa, da;
-        qa.w = *reinterpret_cast<const u32x4*>(qs + (qb * 32 + r) * C::ROW + ks * 16 + g * 8);
-        da.w = *reinterpret_cast<const u32x4*>(os + (qb * 32 + r) * C::ROW + ks * 16 + g * 8);
+        qa.w = *reinterpret_cast<const u32x4*>(qs + swz_off<D>(qb * 32 + r, ks * 16 + g * 8));
+        da.w = *reinterpret_cast<const u32x4*>(os + swz_off<D>(qb * 32 + r, ks * 16 + g * 8));
         sacc[qb] = mfma32x32x16<false>(qa, kf[ks], sacc[qb]);
         pacc[qb] = mfma32x32x16<false>(da, vf[ks], pacc[qb]);
       }
@@ -361,8 +370,8 @@ __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs 
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
           Frag16 ot, qt;
-          ot.w = lds_tr_frag(os, C::ROW, row, row + 8, db * 32);
-          qt.w = lds_tr_frag(qs, C::ROW, row, row + 8, db * 32);
+          ot.w = lds_tr_frag_swz<D>(os, row, row + 8, db * 32);
+          qt.w = lds_tr_frag_swz<D>(qs, row, row + 8, db * 32);
           dvacc[db] = mfma32x32x16<false>(ot, pfr[qb][h], dvacc[db]);
           dkacc[db] = mfma32x32x16<false>(qt, dsf[qb][h], dkacc[db]);
         }
@@ -370,23 +379,24 @@ __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs 
     }
   };
 
-  // Prologue: stage the first query tile, retire every earlier load (the K/V operands) with an
-  // explicit wait, then start the second tile. All loads and LDS writes in the loop are
-  // unconditional (tiles past N read zeros; their math is skipped), so the compiler counts
-  // outstanding loads exactly and never waits on a prefetch before the math.
-  load_tile(0, step_i0(0));
-  store_tile(0, 0, step_i0(0));
+  // Prologue: stage the first query tile and retire every earlier load (the K/V operands). Each
+  // step then starts the loads of the next tile into the other stage (whose previous tile's math
+  // ended before the last barrier), does its math, waits for the loads and publishes the tile.
+  // Tiles past N read zeros; their math is skipped.
+  issue_tile(0, step_i0(0));
   wait_vmem_all();
-  load_tile(1, step_i0(1));
+  store_vec(0, step_i0(0));
   __syncthreads();
   for (int step = 0; step < n_live; step += 2) {
-    load_tile(0, step_i0(step + 2));
+    issue_tile(1, step_i0(step + 1));
     step_math(0, step_i0(step));
-    store_tile(1, 1, step_i0(step + 1));
+    wait_vmem_all();
+    store_vec(1, step_i0(step + 1));
     __syncthreads();
-    load_tile(1, step_i0(step + 3));
+    issue_tile(0, step_i0(step + 2));
     step_math(1, step_i0(step + 1));
-    store_tile(0, 0, step_i0(step + 2));
+    wait_vmem_all();
+    store_vec(0, step_i0(step + 2));
     __syncthreads();
   }
 
@@ -415,16 +425,16 @@ __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs 
 template <int D>
 struct Dq {
   static constexpr int NT = 256;   // 4 waves x 32 queries
+  static constexpr int NW = 4;
   static constexpr int BR = 128;   // queries per workgroup
   static constexpr int BC = 64;    // keys per K/V tile
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int ROW = D + kLdsPad;
-  static constexpr int TILE = BC * ROW;
+  static constexpr int TILE = BC * D;     // swizzled rows, no padding
   static constexpr int STAGE = 2 * TILE;  // K then V
   static constexpr int LDS_BYTES = 2 * STAGE * 2;
-  static constexpr int CHUNKS = BC * D / 8 / NT;
-  static constexpr int MIN_WG = (D == 64) ? 2 : 1;
+  static constexpr int LD_INSTR = BC * D * 2 / 1024;  // 1 KB direct loads per tile and tensor
+  static constexpr int MIN_WG = (D == 64) ? 3 : 2;
 };
 
 template <int D, bool IS_BF16, bool G_F32, bool CAUSAL, bool DROP, bool SPARSE>
@@ -494,36 +504,35 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
     return n * C::BC;
   };
 
-  u32x4 kreg[2][C::CHUNKS], vreg[2][C::CHUNKS];
-  auto load_tile = [&](int set, int j0) {
+  // K and V tiles by direct buffer->LDS loads into swizzled rows (swz_off); both tensors'
+  // rows are placed in perm_row order (LDS row R holds key row_key(R)), since both are A
+  // operands whose accumulator rows must map to keys 16*(i/8) + 8*g + i%8. Lane l of 1 KB load
+  // t deposits 16 bytes at element 512 t + 8 l of the tile.
+  constexpr int LPW = C::LD_INSTR / C::NW;  // loads per wave and tensor
+  uint32_t toff[LPW];
 #pragma unroll
-    for (int u = 0; u < C::CHUNKS; ++u) {
-      const uint32_t off = (uint32_t)(j0 * D + (tid + u * C::NT) * 8) * 2;
-      kreg[set][u] = buf_ld16(krs, off);
-      vreg[set][u] = buf_ld16(vrs, off);
-    }
-  };
-  // K and V rows both go to LDS in perm_row order: both are A operands whose accumulator rows
-  // must map to keys 16*(i/8) + 8*g + i%8.
-  auto store_tile = [&](int set, int stage) {
+  for (int i = 0; i < LPW; ++i) {
+    const int e = (wave + i * C::NW) * 512 + lane * 8;
+    const int R = e / D;
+    const int cch = ((e % D) >> 3) ^ swz(R);
+    toff[i] = (uint32_t)(((R & ~31) + row_key(R & 31)) * D + cch * 8) * 2;
+  }
+  auto issue_tile = [&](int stage, int j0) {
     uint16_t* ks_ = smem + stage * C::STAGE;
     uint16_t* vs_ = ks_ + C::TILE;
+    const uint32_t base = (uint32_t)j0 * D * 2;
 #pragma unroll
-    for (int u = 0; u < C::CHUNKS; ++u) {
-      const int chunk = tid + u * C::NT;
-      const int kk = chunk / (D / 8), cc = chunk % (D / 8);
-      const int row = (kk & ~31) + perm_row(kk & 31);
-      st16(ks_ + row * C::ROW + cc * 8, kreg[set][u]);
-      st16(vs_ + row * C::ROW + cc * 8, vreg[set][u]);
+    for (int i = 0; i < LPW; ++i) {
+      const int t = wave + i * C::NW;
+      buf_ld16_lds(krs, base + toff[i], ks_ + t * 512);
+      buf_ld16_lds(vrs, base + toff[i], vs_ + t * 512);
     }
   };
 
-  load_tile(0, tile_j0(0));
-  store_tile(0, 0);
+  issue_tile(0, tile_j0(0));
   wait_vmem_all();
   // Rows beyond N, and rows that saw no key (LSE = -inf, block-sparse only): P = 0.
   const float lse2 = (qrow < N && lse_raw != -INFINITY) ? lse_raw * kLog2e : INFINITY;
-  load_tile(1, tile_j0(1));
   __syncthreads();
 
   auto tile_math = [&](int stage, int j0) {
@@ -545,8 +554,8 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         Frag16 ka, va;
-        ka.w = *reinterpret_cast<const u32x4*>(ks_ + (kb * 32 + r) * C::ROW + ks * 16 + g * 8);
-        va.w = *reinterpret_cast<const u32x4*>(vs_ + (kb * 32 + r) * C::ROW + ks * 16 + g * 8);
+        ka.w = *reinterpret_cast<const u32x4*>(ks_ + swz_off<D>(kb * 32 + r, ks * 16 + g * 8));
+        va.w = *reinterpret_cast<const u32x4*>(vs_ + swz_off<D>(kb * 32 + r, ks * 16 + g * 8));
         sacc[kb] = mfma32x32x16<false>(ka, qf[ks], sacc[kb]);
         pacc[kb] = mfma32x32x16<false>(va, of[ks], pacc[kb]);
       }
@@ -599,7 +608,7 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
           Frag16 kt;
-          kt.w = lds_tr_frag(ks_, C::ROW, row, row + 8, db * 32);
+          kt.w = lds_tr_frag_swz<D>(ks_, row, row + 8, db * 32);
           dqacc[db] = mfma32x32x16<false>(kt, dsf[kb][h], dqacc[db]);
         }
       }
@@ -607,13 +616,13 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
   };
 
   for (int jt = 0; jt < n_live; jt += 2) {
-    load_tile(0, tile_j0(jt + 2));
+    issue_tile(1, tile_j0(jt + 1));
     tile_math(0, tile_j0(jt));
-    store_tile(1, 1);
+    wait_vmem_all();
     __syncthreads();
-    load_tile(1, tile_j0(jt + 3));
+    issue_tile(0, tile_j0(jt + 2));
     tile_math(1, tile_j0(jt + 1));
-    store_tile(0, 0);
+    wait_vmem_all();
     __syncthreads();
   }
 

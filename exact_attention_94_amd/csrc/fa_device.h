@@ -15,13 +15,6 @@
 
 namespace fa {
 
-// Padding (in 16-bit elements) added to every row of a staged LDS tile, so that the 32 rows an
-// MFMA operand read touches start on different banks. Must keep rows 16-byte aligned.
-#ifndef FA_LDS_PAD
-#define FA_LDS_PAD 8
-#endif
-constexpr int kLdsPad = FA_LDS_PAD;
-static_assert(kLdsPad % 8 == 0, "LDS rows must stay 16-byte aligned");
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -99,24 +92,47 @@ __device__ __forceinline__ float halves_sum(float x) {
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-// MFMA operand (8 x 16-bit, A or B) for lane l = 32*g + n, built from a row-major LDS tile X
-// (`stride` elements per row) with two ds_read_b64_tr_b16:
+
+// Swizzled tile layout (rows of D 16-bit elements, no padding): logical 16-byte chunk c of row r
+// is stored at chunk c ^ swz(r). swz is a bijection on r mod 8, so the eight rows an MFMA
+// operand read (ds_read_b128) touches at one chunk land on eight different chunks, and it puts
+// two of every four consecutive rows in each half of the 128-byte bank window, which balances
+// the transposed reads (ds_read_b64_tr_b16: four rows x 64 bytes per 16 lanes).
+__device__ __forceinline__ int swz(int row) { return ((row & 1) << 2) | ((row >> 1) & 3); }
+template <int D>
+__device__ __forceinline__ int swz_off(int row, int col) {
+  return row * D + ((((col >> 3) ^ swz(row)) << 3) | (col & 7));
+}
+
+// MFMA operand (8 x 16-bit, A or B) for lane l = 32*g + n, built from a swizzled LDS tile X of
+// D-element rows with two ds_read_b64_tr_b16:
 //   slots 0..3 = X[row_lo + s][col0 + n],   slots 4..7 = X[row_hi + s - 4][col0 + n],
 // where row_lo / row_hi already include this lane's g. ds_read_b64_tr_b16 works on groups of 16
 // lanes: output lane i of a group receives, in slot k, element i % 4 of the 8 bytes addressed
 // by lane 4k + i/4 of that group. Lane 4k + j therefore addresses row base + k, columns
-// col0 + 16*(n / 16) + 4j .. +3, and output lane i gets column col0 + 16*(n / 16) + i = col0 + n.
-__device__ __forceinline__ u32x4 lds_tr_frag(const uint16_t* tile, int stride, int row_lo,
-                                             int row_hi, int col0) {
+// col0 + 16*(n / 16) + 4j .. +3 (8 bytes inside one 16-byte chunk, so the chunk swizzle keeps
+// them together), and output lane i gets column col0 + 16*(n / 16) + i = col0 + n.
+template <int D>
+__device__ __forceinline__ u32x4 lds_tr_frag_swz(const uint16_t* tile, int row_lo, int row_hi,
+                                                 int col0) {
   const int lane = threadIdx.x & 63;
   const int col = col0 + (lane & 16) + 4 * (lane & 3);
   const int dr = (lane >> 2) & 3;
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_i16x4*)(tile + (row_lo + dr) * stride + col));
+      (lds_i16x4*)(tile + swz_off<D>(row_lo + dr, col)));
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_i16x4*)(tile + (row_hi + dr) * stride + col));
+      (lds_i16x4*)(tile + swz_off<D>(row_hi + dr, col)));
   const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
   return u32x4{a[0], a[1], b[0], b[1]};
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from a buffer straight into LDS: lane l's data lands at lds + 16 * l
+// (lds must be the same for the whole wave). Out-of-range reads deposit zeros.
+__device__ __forceinline__ void buf_ld16_lds(__amdgpu_buffer_rsrc_t r, uint32_t byte_off,
+                                             uint16_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, byte_off, 0, 0, 0);
 }
 
 // Buffer resource over [base, base + bytes): 16-byte loads through it are branch-free and

@@ -20,8 +20,10 @@
 //     B operand (no LDS round trip); V stays in key order in LDS and its transposed operand is
 //     read with ds_read_b64_tr_b16;
 //   * exp2 with scale*log2(e) folded into one FMA per score;
-//   * K and V^T tiles are double-buffered in LDS (one barrier per K/V tile), the next tile's
-//     global loads are issued before the current tile's math;
+//   * K and V tiles are double-buffered in LDS (one barrier per K/V tile) and filled by direct
+//     buffer->LDS loads, issued for the next tile before the current tile's math: no staging
+//     registers, no LDS write instructions. Tile rows are unpadded and swizzled (swz_off), which
+//     keeps both the row reads of K and the transposed reads of V free of bank conflicts;
 //   * workgroups are ordered longest-first for causal masks and grouped per XCD so that the
 //     query tiles of one (b, h) share an L2.
 #include "fa_device.h"
@@ -50,10 +52,12 @@ __device__ __forceinline__ void map_block(int bid, int n_tiles, int bh_total, bo
   }
 }
 
-// LDS row of key kk (0..31 within a 32-key block) such that accumulator row r of the S^T MFMA
-// holds key 16*(a/2) + 8*b + 4*(a%2) + c for r = 8a + 4b + c. Inverse of that map.
-__device__ __forceinline__ int krow_of_key(int kk) {
-  return 8 * (2 * (kk >> 4) + ((kk >> 2) & 1)) + 4 * ((kk >> 3) & 1) + (kk & 3);
+// Key held by LDS row R (0..31 within a 32-key block) of a K tile: rows are filled so that
+// accumulator row r = 8a + 4b + c of the S^T MFMA holds key 16*(a/2) + 8*b + 4*(a%2) + c, which
+// makes accumulator slot i of lane group g hold key 16*(i/8) + 8*g + i%8 (contiguous runs of 8
+// that feed the P.V MFMA directly).
+__device__ __forceinline__ int key_of_krow(int R) {
+  return 16 * (R >> 4) + 8 * ((R >> 2) & 1) + 4 * ((R >> 3) & 1) + (R & 3);
 }
 
 // Keys per K/V tile of the 16-bit forward kernel.
@@ -70,11 +74,11 @@ struct Fwd16 {
   static constexpr int KB = BC / 32;      // 32-key MFMA blocks per tile
   static constexpr int KS = D / 16;       // contraction steps of S^T = K Q^T
   static constexpr int DB = D / 32;       // 32-row blocks of O^T
-  static constexpr int KROW = D + kLdsPad;      // K and V tile row stride in LDS (elements)
+  static constexpr int KROW = D;          // K and V tile rows in LDS: swizzled, no padding
   static constexpr int KTILE = BC * KROW;
+  static constexpr int LD_INSTR = BC * D * 2 / 1024;  // 1 KB direct loads per tile and tensor
   static constexpr int STAGE = 2 * KTILE;  // K then V, elements per LDS stage
   static constexpr int LDS_BYTES = 2 * STAGE * 2;
-  static constexpr int KCHUNKS = BC * D / 8 / NT;  // 16-byte chunks per thread per tensor
 };
 
 // Queries per wave (32 per MFMA column block). Two blocks halve the LDS reads per MFMA but, at
@@ -160,32 +164,31 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
     return n * C::BC;
   };
 
-  // Global -> register staging of one K/V tile (keys beyond N read as zeros). K rows go to LDS
-  // in the permuted order of krow_of_key; V rows stay in key order (the P.V operand is read
-  // transposed by ds_read_b64_tr_b16).
-  // Two register sets, so that the loads for tile j+2 are in flight while tile j+1 (loaded one
-  // iteration earlier) is written to LDS: each load has two iterations to arrive.
-  u32x4 kreg[2][C::KCHUNKS], vreg[2][C::KCHUNKS];
-  auto load_tile = [&](int set, int j0) {
+  // Global -> LDS staging of one K/V tile by direct (LDS-destination) buffer loads: wave w
+  // issues the 1 KB loads t = w, w + 4, ... of each tensor; lane l of load t deposits 16 bytes at
+  // element 512 t + 8 l of the tile, i.e. LDS row R = (512 t + 8 l) / D, physical chunk p. That
+  // slot holds logical chunk p ^ swz(R) of the key stored on row R: key R for V, and for K the
+  // key given by key_of_krow. Keys beyond N read as zeros.
+  constexpr int LPW = C::LD_INSTR / C::NW;  // loads per wave and tensor
+  uint32_t koff[LPW], voff[LPW];
 #pragma unroll
-    for (int i = 0; i < C::KCHUNKS; ++i) {
-      const int chunk = tid + i * C::NT;
-      const uint32_t off = (uint32_t)(j0 * D + chunk * 8) * 2;
-      kreg[set][i] = buf_ld16(krs, off);
-      vreg[set][i] = buf_ld16(vrs, off);
-    }
-  };
-  auto store_tile = [&](int set, int stage) {
+  for (int i = 0; i < LPW; ++i) {
+    const int e = (wave + i * C::NW) * 512 + lane * 8;
+    const int R = e / D, pch = (e % D) >> 3;
+    const int cch = pch ^ swz(R);
+    const int kkey = (R & ~31) + key_of_krow(R & 31);
+    koff[i] = (uint32_t)(kkey * D + cch * 8) * 2;
+    voff[i] = (uint32_t)(R * D + cch * 8) * 2;
+  }
+  auto issue_tile = [&](int stage, int j0) {
     uint16_t* ks_ = smem + stage * C::STAGE;
     uint16_t* vs_ = ks_ + C::KTILE;
+    const uint32_t base = (uint32_t)j0 * D * 2;
 #pragma unroll
-    for (int i = 0; i < C::KCHUNKS; ++i) {
-      const int chunk = tid + i * C::NT;
-      const int key = chunk / (D / 8);
-      const int cc = chunk % (D / 8);
-      const int row = (key & ~31) + krow_of_key(key & 31);
-      st16(ks_ + row * C::KROW + cc * 8, kreg[set][i]);
-      st16(vs_ + key * C::KROW + cc * 8, vreg[set][i]);
+    for (int i = 0; i < LPW; ++i) {
+      const int t = wave + i * C::NW;
+      buf_ld16_lds(krs, base + koff[i], ks_ + t * 512);
+      buf_ld16_lds(vrs, base + voff[i], vs_ + t * 512);
     }
   };
 
@@ -209,7 +212,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
 #pragma unroll
           for (int kb = 0; kb < C::KB; ++kb) {
             Frag16 kf;
-            kf.w = *reinterpret_cast<const u32x4*>(ks_ + (kb * 32 + r) * C::KROW + ks * 16 + g * 8);
+            kf.w = *reinterpret_cast<const u32x4*>(ks_ + swz_off<D>(kb * 32 + r, ks * 16 + g * 8));
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
               sacc[kb][qb] = mfma32x32x16<IS_BF16>(kf, qf[qb][ks], sacc[kb][qb]);
@@ -298,7 +301,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
               // A operand V^T: lane (g, r) needs V[kb*32 + 16h + 8g + s][32*db + r], s = 0..7.
               Frag16 vf;
               const int row = kb * 32 + h * 16 + g * 8;
-              vf.w = lds_tr_frag(vs_, C::KROW, row, row + 4, db * 32);
+              vf.w = lds_tr_frag_swz<D>(vs_, row, row + 4, db * 32);
 #pragma unroll
               for (int qb = 0; qb < QB; ++qb)
                 oacc[db][qb] = mfma32x32x16<IS_BF16>(vf, pf[kb][h][qb], oacc[db][qb]);
@@ -313,23 +316,20 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
   // before the loop; tile 1 is then in flight when the loop starts. Every load and LDS write in
   // the loop is unconditional (tiles past the end read zeros and their math is skipped), so the
   // compiler counts outstanding loads exactly.
-  load_tile(0, tile_j0(0));
-  store_tile(0, 0);
+  issue_tile(0, tile_j0(0));
   wait_vmem_all();
-  load_tile(1, tile_j0(1));
   __syncthreads();
 
-  // Iteration jt: start loading tile jt+2, do the math of tile jt, write tile jt+1 (loaded during
-  // the previous iteration) into the other LDS stage, barrier. Unrolled by two so that register
-  // sets and LDS stages are compile-time.
+  // Iteration jt: start the direct loads of tile jt+1 into the other stage (its previous tile's
+  // math ended before the last barrier), do the math of tile jt, wait for the loads, barrier.
   for (int jt = 0; jt < n_live; jt += 2) {
-    load_tile(0, tile_j0(jt + 2));
+    issue_tile(1, tile_j0(jt + 1));
     tile_math(0, tile_j0(jt));
-    store_tile(1, 1);
+    wait_vmem_all();
     __syncthreads();
-    load_tile(1, tile_j0(jt + 3));
+    issue_tile(0, tile_j0(jt + 2));
     tile_math(1, tile_j0(jt + 1));
-    store_tile(0, 0);
+    wait_vmem_all();
     __syncthreads();
   }
 
