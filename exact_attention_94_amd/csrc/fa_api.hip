@@ -23,7 +23,7 @@ fa_status check_shape(int B, int H, int N, int d) {
   // Per-head byte offsets (and the prefetches a few tiles past N) must fit the 32-bit offsets
   // of buffer loads.
   if ((long long)N * d > (1LL << 30)) return FA_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (d != 32 && d != 64 && d != 96 && d != 128) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 

@@ -47,15 +47,22 @@ __device__ __forceinline__ u32x4 to_f16x8(u32x4 v) {
   }
 }
 
+// Threads per row in the preprocess: one per 8 elements, rounded up to a power of two (the
+// row sum is a butterfly over them; the extra threads of d = 96 contribute zero).
+template <int D>
+constexpr int pre_tpr() {
+  return D <= 32 ? 4 : D <= 64 ? 8 : 16;
+}
+
 template <int D, bool IS_BF16, bool O_F32>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, long long rows) {
-  constexpr int TPR = D / 8;  // threads per row, 8 elements each
+  constexpr int TPR = pre_tpr<D>();
   constexpr int RPB = 256 / TPR;
   const int t = threadIdx.x;
   const long long row = (long long)blockIdx.x * RPB + t / TPR;
   const int cc = t % TPR;
   float acc = 0.f;
-  if (row < rows) {
+  if (row < rows && cc < D / 8) {
     const size_t base = (size_t)row * D + cc * 8;
     const u32x4 dw = ld16(static_cast<const uint16_t*>(a.dout) + base);
     float dof[8];
@@ -145,7 +152,7 @@ struct Dkdv {
   static constexpr int STAGE = 2 * TILE + 2 * BQ * 2;  // Q, dO, then LSE*log2e and D (fp32)
   static constexpr int LDS_BYTES = 2 * STAGE * 2;
   static constexpr int LD_INSTR = BQ * D * 2 / 1024;  // 1 KB direct loads per tile and tensor
-  static constexpr int MIN_WG = (D == 64) ? 2 : 1;
+  static constexpr int MIN_WG = (D <= 64) ? 2 : 1;
   // Dropout instances: one 32-bit keep word per (wave, query of the step) after the stages.
   static constexpr int MASK_BYTES = 4 * BQ * 4;
 };
@@ -234,7 +241,7 @@ __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs 
   for (int i = 0; i < LPW; ++i) {
     const int e = (wave + i * C::NW) * 512 + lane * 8;
     const int R = e / D;
-    const int cch = ((e % D) >> 3) ^ swz(R);
+    const int cch = ((e % D) >> 3) ^ swz<D>(R);
     toff[i] = (uint32_t)(((R & ~31) + row_key(R & 31)) * D + cch * 8) * 2;
   }
   float lreg, dreg;
@@ -434,7 +441,7 @@ struct Dq {
   static constexpr int STAGE = 2 * TILE;  // K then V
   static constexpr int LDS_BYTES = 2 * STAGE * 2;
   static constexpr int LD_INSTR = BC * D * 2 / 1024;  // 1 KB direct loads per tile and tensor
-  static constexpr int MIN_WG = (D == 64) ? 3 : 2;
+  static constexpr int MIN_WG = (D <= 64) ? 3 : 2;
 };
 
 template <int D, bool IS_BF16, bool G_F32, bool CAUSAL, bool DROP, bool SPARSE>
@@ -514,7 +521,7 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
   for (int i = 0; i < LPW; ++i) {
     const int e = (wave + i * C::NW) * 512 + lane * 8;
     const int R = e / D;
-    const int cch = ((e % D) >> 3) ^ swz(R);
+    const int cch = ((e % D) >> 3) ^ swz<D>(R);
     toff[i] = (uint32_t)(((R & ~31) + row_key(R & 31)) * D + cch * 8) * 2;
   }
   auto issue_tile = [&](int stage, int j0) {
@@ -648,7 +655,7 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
 template <int D, bool IS_BF16>
 static hipError_t launch_pre(const BwdArgs& a, bool o_f32, hipStream_t s) {
   const long long rows = (long long)a.bh * a.N;
-  constexpr int RPB = 256 / (D / 8);
+  constexpr int RPB = 256 / pre_tpr<D>();
   const int grid = (int)((rows + RPB - 1) / RPB);
   if (o_f32)
     hipLaunchKernelGGL((bwd_pre_kernel<D, IS_BF16, true>), dim3(grid), dim3(256), 0, s, a, rows);
@@ -718,11 +725,20 @@ hipError_t launch_backward(const BwdArgs& a, int d, int in_dtype, int o_dtype, i
   const bool bf = in_dtype == 2;
   const bool o_f32 = o_dtype == 0;
   const bool g_f32 = grad_dtype == 0;
-  if (d == 64)
-    return bf ? launch_all<64, true>(a, o_f32, g_f32, causal, drop, s, ev_before, ev_after)
-              : launch_all<64, false>(a, o_f32, g_f32, causal, drop, s, ev_before, ev_after);
-  return bf ? launch_all<128, true>(a, o_f32, g_f32, causal, drop, s, ev_before, ev_after)
-            : launch_all<128, false>(a, o_f32, g_f32, causal, drop, s, ev_before, ev_after);
+  switch (d) {
+    case 32:
+      return bf ? launch_all<32, true>(a, o_f32, g_f32, causal, drop, s, ev_before, ev_after)
+                : launch_all<32, false>(a, o_f32, g_f32, causal, drop, s, ev_before, ev_after);
+    case 64:
+      return bf ? launch_all<64, true>(a, o_f32, g_f32, causal, drop, s, ev_before, ev_after)
+                : launch_all<64, false>(a, o_f32, g_f32, causal, drop, s, ev_before, ev_after);
+    case 96:
+      return bf ? launch_all<96, true>(a, o_f32, g_f32, causal, drop, s, ev_before, ev_after)
+                : launch_all<96, false>(a, o_f32, g_f32, causal, drop, s, ev_before, ev_after);
+    default:
+      return bf ? launch_all<128, true>(a, o_f32, g_f32, causal, drop, s, ev_before, ev_after)
+                : launch_all<128, false>(a, o_f32, g_f32, causal, drop, s, ev_before, ev_after);
+  }
 }
 
 }  // namespace fa

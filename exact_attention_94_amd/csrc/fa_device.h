@@ -94,14 +94,24 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 
 // Swizzled tile layout (rows of D 16-bit elements, no padding): logical 16-byte chunk c of row r
-// is stored at chunk c ^ swz(r). swz is a bijection on r mod 8, so the eight rows an MFMA
-// operand read (ds_read_b128) touches at one chunk land on eight different chunks, and it puts
-// two of every four consecutive rows in each half of the 128-byte bank window, which balances
-// the transposed reads (ds_read_b64_tr_b16: four rows x 64 bytes per 16 lanes).
-__device__ __forceinline__ int swz(int row) { return ((row & 1) << 2) | ((row >> 1) & 3); }
+// is stored at chunk c ^ swz<D>(r), with the 128-byte window of 32 four-byte banks in mind.
+//  * D a multiple of 64 (rows a multiple of 128 bytes, so every row starts on bank 0): swz is a
+//    bijection of r mod 8 onto 0..7, so the eight rows an MFMA operand read (ds_read_b128)
+//    touches at one chunk land on eight different chunks; and it puts two of every four
+//    consecutive rows in each half of the window, which balances the transposed reads
+//    (ds_read_b64_tr_b16: four rows x 64 bytes per 16 lanes).
+//  * D = 32 or 96 (rows start alternately on bank 0 and bank 16): even and odd rows already fall
+//    in different halves, and swz = (r / 2) mod 4 separates the four even (odd) rows of a
+//    ds_read_b128. It only permutes chunks within aligned groups of four, which the transposed
+//    reads (64 bytes = one aligned group per row) leave intact.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D % 64 == 0) return ((row & 1) << 2) | ((row >> 1) & 3);
+  return (row >> 1) & 3;
+}
 template <int D>
 __device__ __forceinline__ int swz_off(int row, int col) {
-  return row * D + ((((col >> 3) ^ swz(row)) << 3) | (col & 7));
+  return row * D + ((((col >> 3) ^ swz<D>(row)) << 3) | (col & 7));
 }
 
 // MFMA operand (8 x 16-bit, A or B) for lane l = 32*g + n, built from a swizzled LDS tile X of

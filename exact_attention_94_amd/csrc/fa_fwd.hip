@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
   // Global -> LDS staging of one K/V tile by direct (LDS-destination) buffer loads: wave w
   // issues the 1 KB loads t = w, w + 4, ... of each tensor; lane l of load t deposits 16 bytes at
   // element 512 t + 8 l of the tile, i.e. LDS row R = (512 t + 8 l) / D, physical chunk p. That
-  // slot holds logical chunk p ^ swz(R) of the key stored on row R: key R for V, and for K the
+  // slot holds logical chunk p ^ swz<D>(R) of the key stored on row R: key R for V, and for K the
   // key given by key_of_krow. Keys beyond N read as zeros.
   constexpr int LPW = C::LD_INSTR / C::NW;  // loads per wave and tensor
   uint32_t koff[LPW], voff[LPW];
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
   for (int i = 0; i < LPW; ++i) {
     const int e = (wave + i * C::NW) * 512 + lane * 8;
     const int R = e / D, pch = (e % D) >> 3;
-    const int cch = pch ^ swz(R);
+    const int cch = pch ^ swz<D>(R);
     const int kkey = (R & ~31) + key_of_krow(R & 31);
     koff[i] = (uint32_t)(kkey * D + cch * 8) * 2;
     voff[i] = (uint32_t)(R * D + cch * 8) * 2;
@@ -546,23 +546,33 @@ static hipError_t launch32(FwdArgs a, bool causal, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D>
+static hipError_t launch16_d(const FwdArgs& a, bool bf, int o_f32, bool causal, Mode mode,
+                             hipStream_t s) {
+  if (bf) return o_f32 ? launch16_c<D, true, true>(a, causal, mode, s)
+                       : launch16_c<D, true, false>(a, causal, mode, s);
+  return o_f32 ? launch16_c<D, false, true>(a, causal, mode, s)
+               : launch16_c<D, false, false>(a, causal, mode, s);
+}
+
 hipError_t launch_forward(const FwdArgs& a, int d, int in_dtype, int o_f32, bool causal,
-                          Mode drop, hipStream_t s) {
+                          Mode mode, hipStream_t s) {
   if (in_dtype == 0) {
-    if (drop != Mode::kPlain) return hipErrorInvalidValue;  // rejected by the C ABI already
-    return d == 64 ? launch32<64>(a, causal, s) : launch32<128>(a, causal, s);
+    if (mode != Mode::kPlain) return hipErrorInvalidValue;  // rejected by the C ABI already
+    switch (d) {
+      case 32: return launch32<32>(a, causal, s);
+      case 64: return launch32<64>(a, causal, s);
+      case 96: return launch32<96>(a, causal, s);
+      default: return launch32<128>(a, causal, s);
+    }
   }
   const bool bf = in_dtype == 2;
-  if (d == 64) {
-    if (bf) return o_f32 ? launch16_c<64, true, true>(a, causal, drop, s)
-                         : launch16_c<64, true, false>(a, causal, drop, s);
-    return o_f32 ? launch16_c<64, false, true>(a, causal, drop, s)
-                 : launch16_c<64, false, false>(a, causal, drop, s);
+  switch (d) {
+    case 32: return launch16_d<32>(a, bf, o_f32, causal, mode, s);
+    case 64: return launch16_d<64>(a, bf, o_f32, causal, mode, s);
+    case 96: return launch16_d<96>(a, bf, o_f32, causal, mode, s);
+    default: return launch16_d<128>(a, bf, o_f32, causal, mode, s);
   }
-  if (bf) return o_f32 ? launch16_c<128, true, true>(a, causal, drop, s)
-                       : launch16_c<128, true, false>(a, causal, drop, s);
-  return o_f32 ? launch16_c<128, false, true>(a, causal, drop, s)
-               : launch16_c<128, false, false>(a, causal, drop, s);
 }
 
 }  // namespace fa

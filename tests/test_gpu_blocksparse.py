@@ -66,7 +66,7 @@ def _run(fa, t, causal, scale, mask_t):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_blocksparse_sweep(fa, dtype, d, causal):
     import torch

@@ -51,7 +51,7 @@ def _fwd_bwd(fa, t, causal, scale, p, seed, offset, o_f32=True):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_dropout_sweep(fa, dtype, d, causal):
     p, seed, offset = 0.2, 0x1234_5678_9ABC_DEF0, 3

@@ -125,7 +125,7 @@ SWEEP_N = [1, 2, 3, 17, 63, 64, 65, 127, 128, 129, 255, 300]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_forward_sweep(fa, dtype, d, causal):
     for n in SWEEP_N:
@@ -135,7 +135,7 @@ def test_forward_sweep(fa, dtype, d, causal):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_backward_sweep(fa, dtype, d, causal):
     import torch
