@@ -44,6 +44,9 @@ def load(path=LIB_PATH):
     if not os.path.exists(path):
         raise RuntimeError(f"HIP attention library not built: {path} is missing "
                            "(run python -m exact_attention_94_amd.build)")
+    # torch provides the device memory and streams: its HIP runtime must be loaded first so that
+    # the library binds to the same one (otherwise torch's stream handles mean nothing to it).
+    _torch()
     lib = ctypes.CDLL(path)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, vp]

@@ -42,8 +42,8 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src, extra):
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+def _compile(src, extra, build_dir=BUILD_DIR):
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     cmd = [hipcc(), "-c", src, "-o", obj] + compile_flags() + list(extra)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -51,24 +51,25 @@ def _compile(src, extra):
     return obj, res.stderr
 
 
-def build_library(verbose=False, extra_flags=()):
-    """Compile all sources and link libfa.so; returns its path. Always rebuilds."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build_library(verbose=False, extra_flags=(), out=LIB, build_dir=BUILD_DIR):
+    """Compile all sources and link the library (default: libfa.so in the package); returns its
+    path. Always rebuilds. extra_flags reach every hipcc compile (e.g. tuning overrides)."""
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, len(srcs))) as ex:
-        results = list(ex.map(lambda s: _compile(s, extra_flags), srcs))
+        results = list(ex.map(lambda s: _compile(s, extra_flags, build_dir), srcs))
     objs = [o for o, _ in results]
     if verbose:
         for _, err in results:
             if err.strip():
                 print(err, file=sys.stderr)
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

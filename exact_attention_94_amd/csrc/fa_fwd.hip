@@ -28,6 +28,7 @@
 //     query tiles of one (b, h) share an L2.
 #include "fa_device.h"
 #include "fa_kernels.h"
+#include "fa_tune.h"
 
 namespace fa {
 
@@ -60,17 +61,14 @@ __device__ __forceinline__ int key_of_krow(int R) {
   return 16 * (R >> 4) + 8 * ((R >> 2) & 1) + 4 * ((R >> 3) & 1) + (R & 3);
 }
 
-// Keys per K/V tile of the 16-bit forward kernel.
-#ifndef FA_FWD_BC
-#define FA_FWD_BC 64
-#endif
-
-template <int D, bool IS_BF16, bool O_F32, bool CAUSAL, int QB>
+// Tile shape of the 16-bit forward kernel: QB 32-query blocks per wave, BC keys per K/V tile
+// (from the tuning table; block-sparse instances use 64, half a mask block).
+template <int D, int QB, int BC_>
 struct Fwd16 {
   static constexpr int NW = 4;            // waves per workgroup
   static constexpr int NT = NW * 64;      // threads
   static constexpr int BR = NW * QB * 32; // query rows per workgroup
-  static constexpr int BC = FA_FWD_BC;    // keys per K/V tile
+  static constexpr int BC = BC_;          // keys per K/V tile
   static constexpr int KB = BC / 32;      // 32-key MFMA blocks per tile
   static constexpr int KS = D / 16;       // contraction steps of S^T = K Q^T
   static constexpr int DB = D / 32;       // 32-row blocks of O^T
@@ -79,7 +77,13 @@ struct Fwd16 {
   static constexpr int LD_INSTR = BC * D * 2 / 1024;  // 1 KB direct loads per tile and tensor
   static constexpr int STAGE = 2 * KTILE;  // K then V, elements per LDS stage
   static constexpr int LDS_BYTES = 2 * STAGE * 2;
+  static_assert(LD_INSTR % NW == 0, "each wave issues whole 1 KB loads");
 };
+
+template <int D, bool SPARSE>
+constexpr int fwd_bc() {
+  return SPARSE ? 64 : fwd_tile_keys<D>();
+}
 
 // Queries per wave (32 per MFMA column block). Two blocks halve the LDS reads per MFMA but, at
 // 227 VGPRs, allow only 2 waves per SIMD and give half as many workgroups for the causal
@@ -91,7 +95,7 @@ constexpr int fwd_qb() {
 
 template <int D, bool IS_BF16, bool O_F32, bool CAUSAL, int QB, bool DROP, bool SPARSE>
 __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
-  using C = Fwd16<D, IS_BF16, O_F32, CAUSAL, QB>;
+  using C = Fwd16<D, QB, fwd_bc<D, SPARSE>()>;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
   const int tid = threadIdx.x;
@@ -506,7 +510,7 @@ __global__ __launch_bounds__(256, 2) void fwd32_kernel(FwdArgs a) {
 // ----------------------------------------------------------------------------------------
 template <int D, bool IS_BF16, bool O_F32, bool CAUSAL, int QB, bool DROP, bool SPARSE>
 static hipError_t launch16(FwdArgs a, hipStream_t s) {
-  using C = Fwd16<D, IS_BF16, O_F32, CAUSAL, QB>;
+  using C = Fwd16<D, QB, fwd_bc<D, SPARSE>()>;
   a.n_tiles = (a.N + C::BR - 1) / C::BR;
   const int grid = a.n_tiles * a.bh;
   constexpr int lds = C::LDS_BYTES + (SPARSE ? kSparseListBytes : 0);

@@ -1,0 +1,32 @@
+// Tile configuration table of the 16-bit forward kernel: keys per K/V tile for each head
+// dimension ("FlashAttention 为什么不需要存下注意力矩阵" §05, first difference: production kernels
+// pick their block sizes per head dimension, dtype and causality among precompiled
+// configurations, by measurement rather than by formula).
+//
+// Written by exact_attention_94_amd/tune.py from timings on MI355X (gfx950) of the candidate
+// widths 32, 64 and 128 at B=2 H=16 N=4096 causal bf16 (per head dim); each value can be
+// overridden at build time with -DFA_FWD_BC_<d>=<keys>. The block-sparse instances always use
+// 64 keys (half a 128-key mask block).
+#pragma once
+
+#ifndef FA_FWD_BC_32
+#define FA_FWD_BC_32 128
+#endif
+#ifndef FA_FWD_BC_64
+#define FA_FWD_BC_64 128
+#endif
+#ifndef FA_FWD_BC_96
+#define FA_FWD_BC_96 64
+#endif
+#ifndef FA_FWD_BC_128
+#define FA_FWD_BC_128 64
+#endif
+
+namespace fa {
+
+template <int D>
+constexpr int fwd_tile_keys() {
+  return D == 32 ? FA_FWD_BC_32 : D == 64 ? FA_FWD_BC_64 : D == 96 ? FA_FWD_BC_96 : FA_FWD_BC_128;
+}
+
+}  // namespace fa

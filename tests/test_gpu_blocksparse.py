@@ -94,21 +94,27 @@ def test_blocksparse_sweep(fa, dtype, d, causal):
 
 
 def test_all_live_mask_is_bitwise_the_plain_path(fa):
+    """With every block live the block-sparse kernels visit the same tiles in the same order as
+    the plain ones. The forward is compared at d = 128, where the plain forward also uses 64-key
+    tiles (its tuned tile width at d = 64 is 128 keys); the backward at d = 64 and 128, from the
+    same O and LSE."""
     import torch
-    t = inp.draw((2, 2, 600, 64), "bf16", 12, with_do=True)
-    q, k, v, do = (to_device(t[n]) for n in ("q", "k", "v", "do"))
-    nb = (600 + BLOCK - 1) // BLOCK
-    ones = torch.ones((nb, nb), dtype=torch.uint8, device="cuda")
-    for causal in (False, True):
-        o0, l0 = fa.forward(q, k, v, causal=causal, o_dtype=torch.float32)
-        o1, l1 = fa.forward(q, k, v, causal=causal, o_dtype=torch.float32, block_mask=ones)
-        g0 = fa.backward(q, k, v, o0, do, l0, causal=causal, grad_dtype=torch.float32)
-        g1 = fa.backward(q, k, v, o1, do, l1, causal=causal, grad_dtype=torch.float32,
-                         block_mask=ones)
-        torch.cuda.synchronize()
-        assert torch.equal(o0, o1) and torch.equal(l0, l1)
-        for x, y in zip(g0, g1):
-            assert torch.equal(x, y)
+    for d in (64, 128):
+        t = inp.draw((2, 2, 600, d), "bf16", 12 + d, with_do=True)
+        q, k, v, do = (to_device(t[n]) for n in ("q", "k", "v", "do"))
+        nb = (600 + BLOCK - 1) // BLOCK
+        ones = torch.ones((nb, nb), dtype=torch.uint8, device="cuda")
+        for causal in (False, True):
+            o0, l0 = fa.forward(q, k, v, causal=causal, o_dtype=torch.float32)
+            o1, l1 = fa.forward(q, k, v, causal=causal, o_dtype=torch.float32, block_mask=ones)
+            g0 = fa.backward(q, k, v, o0, do, l0, causal=causal, grad_dtype=torch.float32)
+            g1 = fa.backward(q, k, v, o0, do, l0, causal=causal, grad_dtype=torch.float32,
+                             block_mask=ones)
+            torch.cuda.synchronize()
+            if d == 128:
+                assert torch.equal(o0, o1) and torch.equal(l0, l1)
+            for x, y in zip(g0, g1):
+                assert torch.equal(x, y)
 
 
 def test_local_global_pattern_b2h16n4k(fa):
