@@ -18,7 +18,8 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = ra
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_forward", "fa_forward_dropout", "fa_forward_blocksparse", "fa_backward",
+EXPORTS = ("fa_forward", "fa_forward_dropout", "fa_forward_blocksparse", "fa_forward_kv",
+           "fa_backward",
            "fa_backward_dropout", "fa_backward_blocksparse", "fa_backward_workspace_bytes",
            "fa_decode_workspace_bytes", "fa_decode_forward", "fa_profile_backward_main",
            "fa_status_string")
@@ -56,6 +57,8 @@ def load(path=LIB_PATH):
     lib.fa_forward_dropout.restype = i
     lib.fa_forward_blocksparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, vp, i, vp]
     lib.fa_forward_blocksparse.restype = i
+    lib.fa_forward_kv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp]
+    lib.fa_forward_kv.restype = i
     lib.fa_backward_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_backward_workspace_bytes.restype = sz
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, i,
@@ -138,15 +141,19 @@ def forward(q, k, v, scale=None, causal=False, o_dtype=None, out=None, lse=None,
     16-bit inputs). `out` / `lse` may be given to write into existing buffers. With dropout_p
     (not None) the call is fa_forward_dropout with that probability, `seed` and `offset`. With
     block_mask (a uint8 GPU tensor [nb, nb] or [1 or B*H, nb, nb], nb = ceil(N / 128)) the call
-    is fa_forward_blocksparse.
+    is fa_forward_blocksparse. If k and v have another length Nk than q (shape [B, H, Nk, d]),
+    the call is fa_forward_kv: with causal, the queries are the last positions of the Nk keys.
     """
     torch = _torch()
     _check_bhnd("q", q)
-    _check_bhnd("k", k, q.shape)
-    _check_bhnd("v", v, q.shape)
+    _check_bhnd("k", k)
+    _check_bhnd("v", v, k.shape)
+    if tuple(k.shape[:2]) != tuple(q.shape[:2]) or k.shape[3] != q.shape[3]:
+        raise ValueError(f"k has shape {tuple(k.shape)}, expected [B, H, Nk, d] with q's B, H, d")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k and v must share a dtype")
     B, H, N, d = q.shape
+    Nk = k.shape[2]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o_dtype = q.dtype if o_dtype is None else o_dtype
     if out is None:
@@ -159,7 +166,12 @@ def forward(q, k, v, scale=None, causal=False, o_dtype=None, out=None, lse=None,
             scale, int(bool(causal)), dtype_code(q.dtype), dtype_code(out.dtype))
     if dropout_p is not None and block_mask is not None:
         raise ValueError("dropout and a block mask cannot be combined")
-    if block_mask is not None:
+    if Nk != N:
+        if dropout_p is not None or block_mask is not None:
+            raise ValueError("dropout and block masks need Nk = Nq")
+        st = load().fa_forward_kv(*args[:8], Nk, *args[8:], _stream(q))
+        where = "fa_forward_kv"
+    elif block_mask is not None:
         heads = _check_mask(block_mask, q)
         st = load().fa_forward_blocksparse(*args, block_mask.data_ptr(), heads, _stream(q))
         where = "fa_forward_blocksparse"

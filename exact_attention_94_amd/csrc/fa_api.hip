@@ -101,10 +101,12 @@ fa_status check_sparse(const uint8_t* mask, int mask_heads, int B, int H, int N,
   return FA_OK;
 }
 
+// Nk = 0: self-attention (Nk = N). Otherwise N query rows attend to Nk >= 1 keys, the queries
+// being the last N positions of the key sequence when causal (N <= Nk then).
 fa_status forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                        int H, int N, int d, float scale, int causal, fa_dtype in_dtype,
                        fa_dtype o_dtype, const fa::DropParams* drop,
-                       const fa::SparseParams* sparse, void* stream) {
+                       const fa::SparseParams* sparse, void* stream, int Nk = 0) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return FA_ERR_INVALID_ARG;
@@ -115,6 +117,12 @@ fa_status forward_impl(const void* q, const void* k, const void* v, void* o, flo
   if (st != FA_OK) return st;
   if (o_dtype != in_dtype && o_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
   if ((drop || sparse) && in_dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (Nk != 0) {
+    const fa_status sk = check_shape(B, H, Nk, d);
+    if (sk != FA_OK) return sk;
+    if (causal && N > Nk) return FA_ERR_INVALID_ARG;
+    if (in_dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  }
 
   fa::FwdArgs a{};
   fa::Mode mode = fa::Mode::kPlain;
@@ -132,6 +140,8 @@ fa_status forward_impl(const void* q, const void* k, const void* v, void* o, flo
   a.o = o;
   a.lse = lse;
   a.N = N;
+  a.Nk = Nk != 0 ? Nk : N;
+  a.qoff = (Nk != 0 && causal) ? Nk - N : 0;
   a.bh = B * H;
   a.c = log2_scale(scale);
   const hipError_t e = fa::launch_forward(a, d, (int)in_dtype, o_dtype == FA_F32 ? 1 : 0,
@@ -226,6 +236,14 @@ fa_status fa_forward_dropout(const void* q, const void* k, const void* v, void* 
   if (!make_drop(dropout_p, seed, offset, dp)) return FA_ERR_INVALID_ARG;
   return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, in_dtype, o_dtype, &dp,
                       nullptr, stream);
+}
+
+fa_status fa_forward_kv(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                        int H, int Nq, int Nk, int d, float scale, int causal, fa_dtype in_dtype,
+                        fa_dtype o_dtype, void* stream) {
+  if (Nk < 1) return FA_ERR_INVALID_ARG;
+  return forward_impl(q, k, v, o, lse, B, H, Nq, d, scale, causal, in_dtype, o_dtype, nullptr,
+                      nullptr, stream, Nk);
 }
 
 fa_status fa_forward_blocksparse(const void* q, const void* k, const void* v, void* o,

@@ -103,15 +103,19 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
   const int wave = tid >> 6;
   const int g = lane >> 5;
   const int r = lane & 31;
+  // Queries are rows 0 .. N-1 of Q and sit at positions qoff .. qoff + N - 1 of the key sequence
+  // (N keys and qoff = 0 unless the caller gave a longer K/V, Nk = N + qoff keys).
   const int N = a.N;
+  const int Nk = a.Nk;
+  const int qoff = a.qoff;
 
   int bh, tile;
   map_block(blockIdx.x, a.n_tiles, a.bh, CAUSAL, bh, tile);
   const size_t head_off = (size_t)bh * N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const auto qrs = make_rsrc(static_cast<const uint16_t*>(a.q) + head_off, head_bytes);
-  const auto krs = make_rsrc(static_cast<const uint16_t*>(a.k) + head_off, head_bytes);
-  const auto vrs = make_rsrc(static_cast<const uint16_t*>(a.v) + head_off, head_bytes);
+  const size_t kv_off = (size_t)bh * Nk * D;
+  const auto qrs = make_rsrc(static_cast<const uint16_t*>(a.q) + head_off, (uint32_t)N * D * 2);
+  const auto krs = make_rsrc(static_cast<const uint16_t*>(a.k) + kv_off, (uint32_t)Nk * D * 2);
+  const auto vrs = make_rsrc(static_cast<const uint16_t*>(a.v) + kv_off, (uint32_t)Nk * D * 2);
 
   const int qt0 = tile * C::BR;
   const int qw0 = qt0 + wave * QB * 32;  // first query of this wave
@@ -146,7 +150,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
   // |scale| * log2(e); never 0 (the host maps scale 0 to a tiny value).
   const float c = __builtin_fabsf(a.c);
 
-  const int kv_end = CAUSAL ? min(N, qt0 + C::BR) : N;
+  const int kv_end = CAUSAL ? min(Nk, qt0 + qoff + C::BR) : Nk;
   const int n_kt = (kv_end + C::BC - 1) / C::BC;
 
   // Block-sparse: the K/V tiles this query tile visits are those whose 128-key block is live in
@@ -198,7 +202,7 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
 
   // Math of one K/V tile already in LDS stage `stage`.
   auto tile_math = [&](int stage, int j0) {
-      const bool wave_live = (j0 < kv_end) && (!CAUSAL || (j0 <= qw0 + QB * 32 - 1));
+      const bool wave_live = (j0 < kv_end) && (!CAUSAL || (j0 <= qw0 + qoff + QB * 32 - 1));
       if (wave_live) {
         const uint16_t* ks_ = smem + stage * C::STAGE;
         const uint16_t* vs_ = ks_ + C::KTILE;
@@ -223,18 +227,18 @@ __global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
           }
         }
 
-        // ---- mask: keys beyond N, and keys after the query on causal diagonal tiles ----------
-        const bool need_mask = (j0 + C::BC > N) || (CAUSAL && (j0 + C::BC - 1 > qw0));
+        // ---- mask: keys beyond Nk, and keys after the query on causal diagonal tiles ---------
+        const bool need_mask = (j0 + C::BC > Nk) || (CAUSAL && (j0 + C::BC - 1 > qw0 + qoff));
         if (need_mask) {
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
-            const int qrow = qw0 + qb * 32 + r;
+            const int qpos = qw0 + qb * 32 + r + qoff;
 #pragma unroll
             for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
               for (int i = 0; i < 16; ++i) {
                 const int key = j0 + kb * 32 + (i >> 3) * 16 + g * 8 + (i & 7);
-                const bool dead = (key >= N) || (CAUSAL && key > qrow);
+                const bool dead = (key >= Nk) || (CAUSAL && key > qpos);
                 sacc[kb][qb][i] = dead ? -INFINITY : sacc[kb][qb][i];
               }
           }

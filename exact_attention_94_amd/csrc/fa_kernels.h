@@ -23,7 +23,9 @@ struct FwdArgs {
   const void* v;
   void* o;
   float* lse;
-  int N;        // sequence length
+  int N;        // query rows per head (the sequence length unless Nk says otherwise)
+  int Nk;       // keys per head (= N for self-attention)
+  int qoff;     // position of query row 0 in the key sequence (causal alignment), usually 0
   int bh;       // B * H
   int n_tiles;  // query tiles per head (set by the launcher)
   float c;      // scale * log2(e), never 0

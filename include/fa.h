@@ -72,6 +72,19 @@ fa_status fa_forward(const void* q, const void* k, const void* v, void* o, float
                      fa_dtype o_dtype, void* stream);
 
 /*
+ * Forward pass with different query and key lengths (chunked prefill over a K/V cache, or
+ * cross-attention): Nq query rows per head against Nk keys. Same computation as fa_forward, with
+ *   q, o     [B,H,Nq,d];  k, v [B,H,Nk,d];  lse [B,H,Nq]
+ *   causal   1: the queries are the LAST Nq positions of the key sequence, so query row i sees
+ *            keys 0 .. Nk - Nq + i (the top-left rule of fa_forward when Nq = Nk); requires
+ *            Nq <= Nk (otherwise FA_ERR_INVALID_ARG). 0: every query sees all Nk keys.
+ * in_dtype must be FA_F16 or FA_BF16 (FA_ERR_UNSUPPORTED otherwise); other errors as fa_forward.
+ */
+fa_status fa_forward_kv(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                        int H, int Nq, int Nk, int d, float scale, int causal, fa_dtype in_dtype,
+                        fa_dtype o_dtype, void* stream);
+
+/*
  * Bytes of device workspace fa_backward needs for these sizes and dtypes: the row vector
  * D = rowsum(dO * O) (float32 [B,H,N]) and, when in_dtype is FA_BF16, fp16 copies of Q, K, V and
  * dO (4 x [B,H,N,d] 16-bit) used as the MFMA operands. grad_dtype does not change the size but is

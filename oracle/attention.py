@@ -307,20 +307,22 @@ def attn_rows_ref(q, k, v, scale, causal, rows):
 
 
 def attn_decode_ref(q, k, v, scale, causal):
-    """Attention of Nq query rows over Nk >= Nq keys (the decoding case, N_q << N_k).
+    """Attention of Nq query rows over Nk keys (decoding, N_q << N_k; chunked prefill; or, not
+    causal, any cross-attention).
 
     q: [..., Nq, d]; k, v: [..., Nk, d]. Same definition as attn_fwd_ref ([FA-V1] §2.2 steps
     1-3, [FA-why] §03 3.1) with the queries taken as the LAST Nq positions of the sequence: when
-    causal, query i (0-based among the Nq) sees keys j <= Nk - Nq + i, which is the top-left rule
-    of [FA-why] §03 3.2 when Nq = Nk. Returns (O [..., Nq, d], LSE [..., Nq]).
+    causal (which needs Nq <= Nk), query i (0-based among the Nq) sees keys j <= Nk - Nq + i, the
+    top-left rule of [FA-why] §03 3.2 when Nq = Nk; otherwise every query sees all Nk keys.
+    Returns (O [..., Nq, d], LSE [..., Nq]).
     """
     qh, lead = _heads(q)
     kh, _ = _heads(k)
     vh, _ = _heads(v)
     G, nq, _ = qh.shape
     nk = kh.shape[1]
-    if nq > nk:
-        raise ValueError("decoding needs Nq <= Nk")
+    if causal and nq > nk:
+        raise ValueError("causal attention with the queries at the end needs Nq <= Nk")
     o = np.empty((G, nq, vh.shape[-1]))
     lse = np.empty((G, nq))
     for g in range(G):

@@ -224,6 +224,28 @@ def test_decode_workspace_bytes():
     assert dec(ws_bytes=need - 1) == B.FA_ERR_WORKSPACE
 
 
+def fwd_kv(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, H=3, Nq=100, Nk=300, d=64, scale=0.125, causal=1,
+             in_dtype=B.FA_BF16, o_dtype=B.FA_BF16)
+    a.update(kw)
+    return _lib().fa_forward_kv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                                a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"], a["in_dtype"],
+                                a["o_dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Nq=301), B.FA_ERR_INVALID_ARG),          # causal needs Nq <= Nk
+    (dict(Nk=0), B.FA_ERR_INVALID_ARG),
+    (dict(Nq=0), B.FA_ERR_INVALID_ARG),
+    (dict(k=None), B.FA_ERR_INVALID_ARG),
+    (dict(in_dtype=B.FA_F32, o_dtype=B.FA_F32), B.FA_ERR_UNSUPPORTED),
+    (dict(d=80), B.FA_ERR_UNSUPPORTED),
+    (dict(B=1, H=1, Nk=(1 << 24) + 1), B.FA_ERR_INVALID_ARG),
+])
+def test_forward_kv_rejects(kw, status):
+    assert fwd_kv(**kw) == status
+
+
 def test_workspace_bytes():
     lib = _lib()
     ws = lib.fa_backward_workspace_bytes

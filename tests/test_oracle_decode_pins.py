@@ -72,3 +72,19 @@ def test_split_merge_with_chunks_invisible_to_some_queries():
     o0, l0 = attn_fwd_ref(q, k, v, 0.5, True)
     o1, l1 = attn_split_merge_ref(q, k, v, 0.5, True, 16)
     assert np.abs(o0 - o1).max() < 1e-13 and np.abs(l0 - l1).max() < 1e-13
+
+
+def test_noncausal_more_queries_than_keys_brute_force():
+    nq, nk, d, scale = 5, 3, 2, 0.8
+    q, k, v = _rand(16, nq, d), _rand(17, nk, d), _rand(18, nk, d)
+    o, l = attn_decode_ref(q, k, v, scale, False)
+    for i in range(nq):
+        s = [scale * sum(q[i, t] * k[j, t] for t in range(d)) for j in range(nk)]
+        mx = max(s)
+        w = [math.exp(x - mx) for x in s]
+        tot = sum(w)
+        for t in range(d):
+            assert abs(o[i, t] - sum(wj * v[j, t] for j, wj in enumerate(w)) / tot) < 1e-14
+        assert abs(l[i] - (mx + math.log(tot))) < 1e-14
+    with pytest.raises(ValueError):
+        attn_decode_ref(q, k, v, scale, True)
