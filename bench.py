@@ -43,7 +43,8 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "attention fwd/bwd TFLOP/s + % bf16 MFMA peak (B2 H16 N4096 d64 causal)"
 WORKLOAD = "b2h16n4k_d64"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_dkdv_b2h16n4k_d64_traffic.txt")
-BWD_SOURCE = os.path.join(ROOT, "exact_attention_94_amd", "csrc", "fa_bwd.hip")
+KERNEL_SOURCES = tuple(os.path.join(ROOT, "exact_attention_94_amd", "csrc", f)
+                       for f in ("fa_bwd.hip", "fa_device.h", "fa_kernels.h"))
 
 
 def flops(w):
@@ -84,8 +85,16 @@ class HipEvents:
         self.rt.hipEventDestroy(ev)
 
 
-def source_digest(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_digest(paths=KERNEL_SOURCES):
+    """Digest of the code (comments and blank lines dropped) of the sources the dK/dV kernel is
+    built from: a comment edit keeps the measured traffic valid, a code change voids it."""
+    h = hashlib.sha256()
+    for path in paths:
+        for line in open(path, encoding="utf-8"):
+            code = re.sub(r"//.*", "", line).strip()
+            if code:
+                h.update(code.encode() + b"\n")
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():
@@ -96,7 +105,7 @@ def measured_traffic():
     text = open(TRAFFIC_FILE, encoding="utf-8").read()
     m_src = re.search(r"^kernel_source_sha256_16:\s*(\w+)", text, re.M)
     m_tot = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
-    if not (m_src and m_tot) or m_src.group(1) != source_digest(BWD_SOURCE):
+    if not (m_src and m_tot) or m_src.group(1) != source_digest():
         return None
     return float(m_tot.group(1))
 

@@ -25,7 +25,9 @@
 // once to fp16 by bwd_pre (exact while 2^-14 <= |x| <= 65504); P and dS are rounded to fp16,
 // whose 11-bit significand keeps the gradients of long peaked rows inside the error budget that
 // bf16 operands would exceed. Operands that a product needs transposed are read from row-major
-// LDS tiles with ds_read_b64_tr_b16, so every tile is staged once, in one layout.
+// LDS tiles with ds_read_b64_tr_b16, so every tile is staged once, in one layout. Streamed tiles
+// (Q / dO in the dK/dV kernel, K / V in the dQ kernel) reach LDS by direct buffer->LDS loads,
+// issued one step ahead, into unpadded rows with the chunk swizzle of swz_off.
 #include "fa_device.h"
 #include "fa_kernels.h"
 

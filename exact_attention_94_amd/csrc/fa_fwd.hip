@@ -20,6 +20,8 @@
 //     B operand (no LDS round trip); V stays in key order in LDS and its transposed operand is
 //     read with ds_read_b64_tr_b16;
 //   * exp2 with scale*log2(e) folded into one FMA per score;
+//   * K/V tiles hold fwd_tile_keys<D>() keys (a per-head-dim table written by the tuner; 64 for
+//     block-sparse masks);
 //   * K and V tiles are double-buffered in LDS (one barrier per K/V tile) and filled by direct
 //     buffer->LDS loads, issued for the next tile before the current tile's math: no staging
 //     registers, no LDS write instructions. Tile rows are unpadded and swizzled (swz_off), which
