@@ -15,7 +15,8 @@ bool valid_dtype(int t) { return t == FA_F32 || t == FA_F16 || t == FA_BF16; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Shared shape checks. Returns FA_OK or the status to report.
+// Shared shape checks. Returns FA_OK or the status to report. d = 256 passes here; only the
+// plain 16-bit forward provides it (the other entry points reject it themselves).
 fa_status check_shape(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
   const long long elems = (long long)B * H * N * d;
@@ -23,7 +24,7 @@ fa_status check_shape(int B, int H, int N, int d) {
   // Per-head byte offsets (and the prefetches a few tiles past N) must fit the 32-bit offsets
   // of buffer loads.
   if ((long long)N * d > (1LL << 30)) return FA_ERR_INVALID_ARG;
-  if (d != 32 && d != 64 && d != 96 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (d != 32 && d != 64 && d != 96 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 
@@ -117,6 +118,7 @@ fa_status forward_impl(const void* q, const void* k, const void* v, void* o, flo
   if (st != FA_OK) return st;
   if (o_dtype != in_dtype && o_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
   if ((drop || sparse) && in_dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (d == 256 && (drop || sparse || in_dtype == FA_F32)) return FA_ERR_UNSUPPORTED;
   if (Nk != 0) {
     const fa_status sk = check_shape(B, H, Nk, d);
     if (sk != FA_OK) return sk;
@@ -165,7 +167,7 @@ fa_status backward_impl(const void* q, const void* k, const void* v, const void*
   if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
   const fa_status st = check_shape(B, H, N, d);
   if (st != FA_OK) return st;
-  if (in_dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (in_dtype == FA_F32 || d == 256) return FA_ERR_UNSUPPORTED;
   if (o_dtype != in_dtype && o_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
   if (grad_dtype != in_dtype && grad_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
   const WsLayout ws = workspace_layout(B, H, N, d, in_dtype);
@@ -261,7 +263,8 @@ fa_status fa_forward_blocksparse(const void* q, const void* k, const void* v, vo
 
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d, fa_dtype in_dtype,
                                    fa_dtype grad_dtype) {
-  if (check_shape(B, H, N, d) != FA_OK || !valid_dtype(in_dtype) || !valid_dtype(grad_dtype))
+  if (check_shape(B, H, N, d) != FA_OK || d == 256 || !valid_dtype(in_dtype) ||
+      !valid_dtype(grad_dtype))
     return 0;
   return workspace_layout(B, H, N, d, in_dtype).total;
 }

@@ -95,8 +95,15 @@ constexpr int fwd_qb() {
   return 1;
 }
 
+// Waves per SIMD the register allocation must allow: 2, except at d = 256, whose 32-query
+// output accumulator alone is 128 registers (one wave then uses the whole file, AGPRs included).
+template <int D>
+constexpr int fwd_min_waves() {
+  return D >= 256 ? 1 : 2;
+}
+
 template <int D, bool IS_BF16, bool O_F32, bool CAUSAL, int QB, bool DROP, bool SPARSE>
-__global__ __launch_bounds__(256, 2) void fwd16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, fwd_min_waves<D>()) void fwd16_kernel(FwdArgs a) {
   using C = Fwd16<D, QB, fwd_bc<D, SPARSE>()>;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
@@ -577,6 +584,13 @@ hipError_t launch_forward(const FwdArgs& a, int d, int in_dtype, int o_f32, bool
     }
   }
   const bool bf = in_dtype == 2;
+  if (d == 256) {  // plain attention only (the C ABI rejects dropout and block masks here)
+    if (mode != Mode::kPlain) return hipErrorInvalidValue;
+    if (bf) return o_f32 ? launch16_m<256, true, true, false, false>(a, causal, s)
+                         : launch16_m<256, true, false, false, false>(a, causal, s);
+    return o_f32 ? launch16_m<256, false, true, false, false>(a, causal, s)
+                 : launch16_m<256, false, false, false, false>(a, causal, s);
+  }
   switch (d) {
     case 32: return launch16_d<32>(a, bf, o_f32, causal, mode, s);
     case 64: return launch16_d<64>(a, bf, o_f32, causal, mode, s);

@@ -21,12 +21,19 @@
 #ifndef FA_FWD_BC_128
 #define FA_FWD_BC_128 64
 #endif
+#ifndef FA_FWD_BC_256
+#define FA_FWD_BC_256 32
+#endif
 
 namespace fa {
 
 template <int D>
 constexpr int fwd_tile_keys() {
-  return D == 32 ? FA_FWD_BC_32 : D == 64 ? FA_FWD_BC_64 : D == 96 ? FA_FWD_BC_96 : FA_FWD_BC_128;
+  return D == 32    ? FA_FWD_BC_32
+         : D == 64  ? FA_FWD_BC_64
+         : D == 96  ? FA_FWD_BC_96
+         : D == 128 ? FA_FWD_BC_128
+                    : FA_FWD_BC_256;
 }
 
 }  // namespace fa

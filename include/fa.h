@@ -19,7 +19,8 @@
  * vectors are contiguous [B, H, N]. Q, K and V share N (self-attention). Pointers must be
  * device pointers (hipMalloc'd or equivalent) aligned to 16 bytes.
  *
- * Supported: d in {32, 64, 96, 128} (decoding: {64, 128}); N >= 1 (a ragged tail is masked);
+ * Supported: d in {32, 64, 96, 128}, and 256 for the plain 16-bit forward (fa_forward,
+ * fa_forward_kv) only; decoding: d in {64, 128}. N >= 1 (a ragged tail is masked);
  * B, H >= 1 with B*H*N*d < 2^31
  * and N*d <= 2^30;
  * in_dtype in {FA_F32, FA_F16, FA_BF16}; any finite scale; causal in {0, 1}.

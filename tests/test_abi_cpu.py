@@ -79,7 +79,8 @@ def bwd(**kw):
     (dict(in_dtype=7), B.FA_ERR_INVALID_ARG),
     (dict(d=80), B.FA_ERR_UNSUPPORTED),
     (dict(d=16), B.FA_ERR_UNSUPPORTED),
-    (dict(d=256), B.FA_ERR_UNSUPPORTED),
+    (dict(d=512), B.FA_ERR_UNSUPPORTED),
+    (dict(d=256, in_dtype=B.FA_F32, o_dtype=B.FA_F32), B.FA_ERR_UNSUPPORTED),
     (dict(o_dtype=B.FA_F16), B.FA_ERR_UNSUPPORTED),
     (dict(in_dtype=B.FA_F32, o_dtype=B.FA_BF16), B.FA_ERR_UNSUPPORTED),
 ])
@@ -139,6 +140,7 @@ def test_dropout_rejects_bad_probability(p):
 def test_dropout_rejects_like_the_plain_calls():
     assert fwd_drop(q=None) == B.FA_ERR_INVALID_ARG
     assert fwd_drop(d=80) == B.FA_ERR_UNSUPPORTED
+    assert fwd_drop(d=256) == B.FA_ERR_UNSUPPORTED  # d = 256: plain forward only
     # The fp32 forward has no dropout instance.
     assert fwd_drop(in_dtype=B.FA_F32, o_dtype=B.FA_F32) == B.FA_ERR_UNSUPPORTED
     assert bwd_drop(ws=None) == B.FA_ERR_WORKSPACE
@@ -175,6 +177,7 @@ def test_blocksparse_rejects(call):
     assert call(N=65537, B=1, H=1) == B.FA_ERR_UNSUPPORTED
     assert call(in_dtype=B.FA_F32, o_dtype=B.FA_F32) == B.FA_ERR_UNSUPPORTED
     assert call(d=80) == B.FA_ERR_UNSUPPORTED
+    assert call(d=256) == B.FA_ERR_UNSUPPORTED
     assert call(N=0) == B.FA_ERR_INVALID_ARG
     assert call(q=None, heads=6) == B.FA_ERR_INVALID_ARG
 
@@ -257,6 +260,7 @@ def test_workspace_bytes():
     assert ws(2, 3, 100, 64, B.FA_BF16, B.FA_BF16) == 2560 + 4 * e * 2
     assert ws(1, 1, 1, 128, B.FA_F16, B.FA_F16) == 256
     assert ws(1, 1, 1, 80, B.FA_F16, B.FA_F32) == 0
+    assert ws(1, 1, 1, 256, B.FA_F16, B.FA_F32) == 0  # no backward at d = 256
     # Head dims 32 and 96 are provided; the workspace only depends on d through the copies.
     assert ws(1, 1, 1, 96, B.FA_F16, B.FA_F32) == 256
     assert ws(1, 2, 10, 32, B.FA_BF16, B.FA_F32) == 256 + 4 * 2 * 10 * 32 * 2

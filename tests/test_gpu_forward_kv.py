@@ -28,7 +28,7 @@ CASES_FULL = CASES_CAUSAL + [(300, 17), (5, 1)]
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("d", [32, 64, 96, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_forward_kv_sweep(fa, dtype, d, causal):
     import torch

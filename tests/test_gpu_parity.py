@@ -135,6 +135,16 @@ def test_forward_sweep(fa, dtype, d, causal):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_sweep_d256(fa, dtype, causal):
+    """d = 256 (plain 16-bit forward only: one wave per SIMD, accumulators in AGPRs)."""
+    for n in [1, 17, 63, 64, 65, 129, 300]:
+        for (B, H) in ((1, 2), (2, 3)):
+            print(f"  N={n} B={B} H={H}", flush=True)
+            _fwd_case(fa, (B, H, n, 256), dtype, causal, seed=n * 7 + 256)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("d", [32, 64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_backward_sweep(fa, dtype, d, causal):
