@@ -57,13 +57,17 @@ def _scores(qh, kh, scale, causal, visible=None):
     """S = scale * Q K^T for one head; with causal, key index j > query index i is -inf.
 
     [FA-V1] §2.2 step 1 (S = Q K^T, here with the softmax scale folded in, [FA-why] §03 3.3 uses
-    1/sqrt(d)); the causal rule (masked score = -inf) is [FA-why] §03 3.2, last paragraph.
+    1/sqrt(d)); the causal rule (masked score = -inf) is [FA-why] §03 3.2, last paragraph. With
+    fewer query rows than keys (Nq < Nk) the queries are the last Nq positions: row i is at
+    position i + Nk - Nq.
     `visible` (bool [N, N], optional) masks further: scores of invisible keys are -inf.
     """
     s = scale * (qh @ kh.T)
     if causal:
         n_q, n_k = s.shape
-        s[np.triu(np.ones((n_q, n_k), dtype=bool), 1)] = -np.inf
+        if n_q > n_k:
+            raise ValueError("causal attention with the queries at the end needs Nq <= Nk")
+        s[np.triu(np.ones((n_q, n_k), dtype=bool), 1 + n_k - n_q)] = -np.inf
     if visible is not None:
         s[~np.asarray(visible, dtype=bool)] = -np.inf
     return s
@@ -162,7 +166,8 @@ def attn_bwd_ref(q, k, v, do, scale, causal, o=None, keep=None, keep_scale=1.0, 
         dV = P_d^T G,  A = (G V^T) * Z * keep_scale = dL/dP,  and dS, dQ, dK as above.
 
     With a block-sparse visibility mask (`visible`, as in attn_fwd_ref), invisible keys have
-    P = 0; a query that sees no key has zero gradients.
+    P = 0; a query that sees no key has zero gradients. k and v may hold Nk != N rows (the
+    backward of attn_decode_ref: with causal, the N queries are the last positions).
 
     Returns dict with dq, dk, dv ([..., N, d]) and D = rowsum(dP * P) ([..., N]).
     If `o` (the forward output) is given, also returns D_o = rowsum(dO * O), which equals D in
@@ -173,9 +178,10 @@ def attn_bwd_ref(q, k, v, do, scale, causal, o=None, keep=None, keep_scale=1.0, 
     vh, _ = _heads(v)
     doh, _ = _heads(do)
     G, N, d = qh.shape
+    Nk = kh.shape[1]
     dq = np.empty_like(qh)
-    dk = np.empty_like(qh)
-    dv = np.empty_like(qh)
+    dk = np.empty_like(kh)
+    dv = np.empty_like(vh)
     D = np.empty((G, N))
     kp = _keep_heads(keep, G, N)
     vis = _visible_heads(visible, G, N)
@@ -194,8 +200,8 @@ def attn_bwd_ref(q, k, v, do, scale, causal, o=None, keep=None, keep_scale=1.0, 
         dk[g] = scale * (ds.T @ qh[g])
     out = {
         "dq": dq.reshape(lead + (N, d)),
-        "dk": dk.reshape(lead + (N, d)),
-        "dv": dv.reshape(lead + (N, d)),
+        "dk": dk.reshape(lead + (Nk, d)),
+        "dv": dv.reshape(lead + (Nk, vh.shape[-1])),
         "D": D.reshape(lead + (N,)),
     }
     if o is not None:

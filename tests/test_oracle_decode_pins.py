@@ -88,3 +88,33 @@ def test_noncausal_more_queries_than_keys_brute_force():
         assert abs(l[i] - (mx + math.log(tot))) < 1e-14
     with pytest.raises(ValueError):
         attn_decode_ref(q, k, v, scale, True)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_with_fewer_queries_than_keys_matches_finite_differences(causal):
+    """attn_bwd_ref with Nq < Nk is the gradient of attn_decode_ref (queries at the end)."""
+    from oracle import attn_bwd_ref
+    nq, nk, d, scale = 3, 7, 3, 0.6
+    q, k, v, do = _rand(20, nq, d), _rand(21, nk, d), _rand(22, nk, d), _rand(23, nq, d)
+
+    def loss(qq, kk, vv):
+        o, _ = attn_decode_ref(qq, kk, vv, scale, causal)
+        return float((do * o).sum())
+
+    g = attn_bwd_ref(q, k, v, do, scale, causal)
+    assert g["dq"].shape == (nq, d) and g["dk"].shape == (nk, d)
+    h = 1e-6
+    for name, x in (("dq", q), ("dk", k), ("dv", v)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            a_p = {"dq": (xp, k, v), "dk": (q, xp, v), "dv": (q, k, xp)}[name]
+            a_m = {"dq": (xm, k, v), "dk": (q, xm, v), "dv": (q, k, xm)}[name]
+            num[idx] = (loss(*a_p) - loss(*a_m)) / (2 * h)
+        assert np.abs(num - g[name]).max() < 1e-7
+    if causal:
+        # The first key rows that no query can reach would have zero gradient only if none sees
+        # them; with the queries at the end, the last query sees every key.
+        assert np.abs(g["dk"]).sum() > 0
