@@ -19,7 +19,7 @@ FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 
 # Every symbol include/fa.h declares.
 EXPORTS = ("fa_forward", "fa_forward_dropout", "fa_forward_blocksparse", "fa_forward_kv",
-           "fa_backward",
+           "fa_backward", "fa_backward_kv", "fa_backward_kv_workspace_bytes",
            "fa_backward_dropout", "fa_backward_blocksparse", "fa_backward_workspace_bytes",
            "fa_decode_workspace_bytes", "fa_decode_forward", "fa_profile_backward_main",
            "fa_status_string")
@@ -64,6 +64,11 @@ def load(path=LIB_PATH):
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, i,
                                 vp, sz, vp]
     lib.fa_backward.restype = i
+    lib.fa_backward_kv_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.fa_backward_kv_workspace_bytes.restype = sz
+    lib.fa_backward_kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i,
+                                   i, vp, sz, vp]
+    lib.fa_backward_kv.restype = i
     lib.fa_backward_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i,
                                         i, f, u64, u32, vp, sz, vp]
     lib.fa_backward_dropout.restype = i
@@ -205,20 +210,35 @@ def backward(q, k, v, o, dout, lse, scale=None, causal=False, grad_dtype=None, w
     `workspace` (a uint8 GPU tensor) is allocated when not given; `grads` may supply the three
     output tensors. With dropout_p (not None) the call is fa_backward_dropout, which regenerates
     the forward's keep mask from the same (dropout_p, seed, offset); with block_mask it is
-    fa_backward_blocksparse (the mask given to the forward).
+    fa_backward_blocksparse (the mask given to the forward). If k and v have another length Nk
+    than q, the call is fa_backward_kv (the backward of fa_forward_kv); dK and dV are then
+    [B, H, Nk, d].
     """
     torch = _torch()
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+    for name, t in (("q", q), ("o", o), ("dout", dout)):
         _check_bhnd(name, t, q.shape)
+    _check_bhnd("k", k)
+    _check_bhnd("v", v, k.shape)
+    if tuple(k.shape[:2]) != tuple(q.shape[:2]) or k.shape[3] != q.shape[3]:
+        raise ValueError(f"k has shape {tuple(k.shape)}, expected [B, H, Nk, d] with q's B, H, d")
     B, H, N, d = q.shape
+    Nk = k.shape[2]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     grad_dtype = q.dtype if grad_dtype is None else grad_dtype
     gcode = dtype_code(grad_dtype)
     if grads is None:
-        grads = tuple(torch.empty((B, H, N, d), dtype=grad_dtype, device=q.device)
-                      for _ in range(3))
+        grads = (torch.empty((B, H, N, d), dtype=grad_dtype, device=q.device),
+                 torch.empty((B, H, Nk, d), dtype=grad_dtype, device=q.device),
+                 torch.empty((B, H, Nk, d), dtype=grad_dtype, device=q.device))
     dq, dk, dv = grads
-    need = workspace_bytes(B, H, N, d, dtype_code(q.dtype), gcode)
+    _check_bhnd("dq", dq, q.shape)
+    _check_bhnd("dk", dk, k.shape)
+    _check_bhnd("dv", dv, k.shape)
+    if Nk != N:
+        need = int(load().fa_backward_kv_workspace_bytes(B, H, N, Nk, d, dtype_code(q.dtype),
+                                                         gcode))
+    else:
+        need = workspace_bytes(B, H, N, d, dtype_code(q.dtype), gcode)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
@@ -226,7 +246,13 @@ def backward(q, k, v, o, dout, lse, scale=None, causal=False, grad_dtype=None, w
             int(bool(causal)), dtype_code(q.dtype), dtype_code(o.dtype), gcode)
     if dropout_p is not None and block_mask is not None:
         raise ValueError("dropout and a block mask cannot be combined")
-    if block_mask is not None:
+    if Nk != N:
+        if dropout_p is not None or block_mask is not None:
+            raise ValueError("dropout and block masks need Nk = Nq")
+        st = load().fa_backward_kv(*args[:12], Nk, *args[12:], workspace.data_ptr(),
+                                   workspace.numel(), _stream(q))
+        where = "fa_backward_kv"
+    elif block_mask is not None:
         heads = _check_mask(block_mask, q)
         st = load().fa_backward_blocksparse(*args, block_mask.data_ptr(), heads,
                                             workspace.data_ptr(), workspace.numel(), _stream(q))

@@ -55,18 +55,19 @@ bool make_drop(float p, uint64_t seed, uint32_t offset, fa::DropParams& dp) {
   return true;
 }
 
-// Workspace: D (fp32 [B,H,N]) | for bf16 inputs, fp16 copies of Q, K, V, dO ([B,H,N,d] each),
-// 256-byte aligned.
+// Workspace: D (fp32 [B,H,Nq]) | for bf16 inputs, fp16 copies of Q ([B,H,Nq,d]), K and V
+// ([B,H,Nk,d] each) and dO ([B,H,Nq,d]); the copies start 256 bytes aligned.
 struct WsLayout {
-  size_t f16_off, total;
+  size_t f16_off, q_elems, k_elems, total;
 };
 
-WsLayout workspace_layout(int B, int H, int N, int d, fa_dtype in_dtype) {
-  const size_t rows = (size_t)B * H * N;
-  const size_t elems = rows * (size_t)d;
+WsLayout workspace_layout(int B, int H, int Nq, int Nk, int d, fa_dtype in_dtype) {
+  const size_t rows = (size_t)B * H * Nq;
   WsLayout w;
+  w.q_elems = rows * (size_t)d;
+  w.k_elems = (size_t)B * H * Nk * (size_t)d;
   w.f16_off = round_up(rows * sizeof(float), 256);
-  w.total = w.f16_off + ((in_dtype == FA_BF16) ? 4 * elems * 2 : 0);
+  w.total = w.f16_off + ((in_dtype == FA_BF16) ? (2 * w.q_elems + 2 * w.k_elems) * 2 : 0);
   return w;
 }
 
@@ -151,12 +152,13 @@ fa_status forward_impl(const void* q, const void* k, const void* v, void* o, flo
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+// Nk = 0: self-attention (Nk = N); otherwise as in forward_impl (plain mode only).
 fa_status backward_impl(const void* q, const void* k, const void* v, const void* o,
                         const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
                         int H, int N, int d, float scale, int causal, fa_dtype in_dtype,
                         fa_dtype o_dtype, fa_dtype grad_dtype, const fa::DropParams* drop,
                         const fa::SparseParams* sparse, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+                        void* stream, int Nk = 0) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
       !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
@@ -170,7 +172,14 @@ fa_status backward_impl(const void* q, const void* k, const void* v, const void*
   if (in_dtype == FA_F32 || d == 256) return FA_ERR_UNSUPPORTED;
   if (o_dtype != in_dtype && o_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
   if (grad_dtype != in_dtype && grad_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
-  const WsLayout ws = workspace_layout(B, H, N, d, in_dtype);
+  if (Nk != 0) {
+    const fa_status sk = check_shape(B, H, Nk, d);
+    if (sk != FA_OK) return sk;
+    if (causal && N > Nk) return FA_ERR_INVALID_ARG;
+    if (drop || sparse) return FA_ERR_UNSUPPORTED;
+  }
+  const int nk = Nk != 0 ? Nk : N;
+  const WsLayout ws = workspace_layout(B, H, N, nk, d, in_dtype);
   if (!workspace || !aligned16(workspace) || workspace_bytes < ws.total) return FA_ERR_WORKSPACE;
   char* wsb = static_cast<char*>(workspace);
 
@@ -182,16 +191,17 @@ fa_status backward_impl(const void* q, const void* k, const void* v, const void*
   a.dout = dout;
   a.lse = lse;
   a.delta = static_cast<float*>(workspace);
-  a.elems = (size_t)B * H * N * d;
   if (in_dtype == FA_BF16) {
     uint16_t* f16 = reinterpret_cast<uint16_t*>(wsb + ws.f16_off);
-    a.ws16 = f16;
-    a.q16 = f16;
-    a.k16 = f16 + a.elems;
-    a.v16 = f16 + 2 * a.elems;
-    a.do16 = f16 + 3 * a.elems;
+    a.ws_q = f16;
+    a.ws_k = a.ws_q + ws.q_elems;
+    a.ws_v = a.ws_k + ws.k_elems;
+    a.ws_do = a.ws_v + ws.k_elems;
+    a.q16 = a.ws_q;
+    a.k16 = a.ws_k;
+    a.v16 = a.ws_v;
+    a.do16 = a.ws_do;
   } else {
-    a.ws16 = nullptr;
     a.q16 = static_cast<const uint16_t*>(q);
     a.k16 = static_cast<const uint16_t*>(k);
     a.v16 = static_cast<const uint16_t*>(v);
@@ -201,6 +211,8 @@ fa_status backward_impl(const void* q, const void* k, const void* v, const void*
   a.dk = dk;
   a.dv = dv;
   a.N = N;
+  a.Nk = nk;
+  a.qoff = (Nk != 0 && causal) ? Nk - N : 0;
   a.bh = B * H;
   a.scale = scale;
   a.c = log2_scale(scale);
@@ -266,7 +278,15 @@ size_t fa_backward_workspace_bytes(int B, int H, int N, int d, fa_dtype in_dtype
   if (check_shape(B, H, N, d) != FA_OK || d == 256 || !valid_dtype(in_dtype) ||
       !valid_dtype(grad_dtype))
     return 0;
-  return workspace_layout(B, H, N, d, in_dtype).total;
+  return workspace_layout(B, H, N, N, d, in_dtype).total;
+}
+
+size_t fa_backward_kv_workspace_bytes(int B, int H, int Nq, int Nk, int d, fa_dtype in_dtype,
+                                      fa_dtype grad_dtype) {
+  if (check_shape(B, H, Nq, d) != FA_OK || check_shape(B, H, Nk, d) != FA_OK || d == 256 ||
+      !valid_dtype(in_dtype) || !valid_dtype(grad_dtype))
+    return 0;
+  return workspace_layout(B, H, Nq, Nk, d, in_dtype).total;
 }
 
 fa_status fa_backward(const void* q, const void* k, const void* v, const void* o,
@@ -276,6 +296,17 @@ fa_status fa_backward(const void* q, const void* k, const void* v, const void* o
                       size_t workspace_bytes, void* stream) {
   return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, in_dtype,
                        o_dtype, grad_dtype, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+fa_status fa_backward_kv(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                         int H, int Nq, int Nk, int d, float scale, int causal,
+                         fa_dtype in_dtype, fa_dtype o_dtype, fa_dtype grad_dtype,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (Nk < 1) return FA_ERR_INVALID_ARG;
+  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, Nq, d, scale, causal, in_dtype,
+                       o_dtype, grad_dtype, nullptr, nullptr, workspace, workspace_bytes, stream,
+                       Nk);
 }
 
 fa_status fa_backward_dropout(const void* q, const void* k, const void* v, const void* o,

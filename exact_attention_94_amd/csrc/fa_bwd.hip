@@ -56,16 +56,19 @@ constexpr int pre_tpr() {
   return D <= 32 ? 4 : D <= 64 ? 8 : 16;
 }
 
+// Row r < rows_q: D[r] = rowsum(dO * O) and, for bf16 inputs, fp16 copies of Q and dO; row
+// r < rows_k: fp16 copies of K and V (bf16 inputs). Rows are flattened over (b, h).
 template <int D, bool IS_BF16, bool O_F32>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, long long rows) {
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, long long rows_q,
+                                                      long long rows_k) {
   constexpr int TPR = pre_tpr<D>();
   constexpr int RPB = 256 / TPR;
   const int t = threadIdx.x;
   const long long row = (long long)blockIdx.x * RPB + t / TPR;
   const int cc = t % TPR;
+  const size_t base = (size_t)row * D + cc * 8;
   float acc = 0.f;
-  if (row < rows && cc < D / 8) {
-    const size_t base = (size_t)row * D + cc * 8;
+  if (row < rows_q && cc < D / 8) {
     const u32x4 dw = ld16(static_cast<const uint16_t*>(a.dout) + base);
     float dof[8];
 #pragma unroll
@@ -88,15 +91,19 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, long long rows)
       }
     }
     if constexpr (IS_BF16) {
-      st16(a.ws16 + base, to_f16x8<true>(ld16(static_cast<const uint16_t*>(a.q) + base)));
-      st16(a.ws16 + a.elems + base, to_f16x8<true>(ld16(static_cast<const uint16_t*>(a.k) + base)));
-      st16(a.ws16 + 2 * a.elems + base, to_f16x8<true>(ld16(static_cast<const uint16_t*>(a.v) + base)));
-      st16(a.ws16 + 3 * a.elems + base, to_f16x8<true>(dw));
+      st16(a.ws_q + base, to_f16x8<true>(ld16(static_cast<const uint16_t*>(a.q) + base)));
+      st16(a.ws_do + base, to_f16x8<true>(dw));
+    }
+  }
+  if constexpr (IS_BF16) {
+    if (row < rows_k && cc < D / 8) {
+      st16(a.ws_k + base, to_f16x8<true>(ld16(static_cast<const uint16_t*>(a.k) + base)));
+      st16(a.ws_v + base, to_f16x8<true>(ld16(static_cast<const uint16_t*>(a.v) + base)));
     }
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && cc == 0) a.delta[row] = acc;
+  if (row < rows_q && cc == 0) a.delta[row] = acc;
 }
 
 // Row placement inside a 32-row block of a staged tile: LDS row r holds element
@@ -170,16 +177,18 @@ __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
   const int g = lane >> 5;
   const int r = lane & 31;
-  const int N = a.N;
+  const int N = a.N;    // query rows
+  const int Nk = a.Nk;  // keys
+  const int qoff = a.qoff;
 
   int bh, kt;
   map_bwd_block(blockIdx.x, a.bh, false, a.n_tiles, bh, kt);
-  const size_t head_off = (size_t)bh * N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const auto qrs = make_rsrc(a.q16 + head_off, head_bytes);
-  const auto krs = make_rsrc(a.k16 + head_off, head_bytes);
-  const auto vrs = make_rsrc(a.v16 + head_off, head_bytes);
-  const auto dors = make_rsrc(a.do16 + head_off, head_bytes);
+  const size_t q_off = (size_t)bh * N * D;
+  const size_t kv_off = (size_t)bh * Nk * D;
+  const auto qrs = make_rsrc(a.q16 + q_off, (uint32_t)N * D * 2);
+  const auto krs = make_rsrc(a.k16 + kv_off, (uint32_t)Nk * D * 2);
+  const auto vrs = make_rsrc(a.v16 + kv_off, (uint32_t)Nk * D * 2);
+  const auto dors = make_rsrc(a.do16 + q_off, (uint32_t)N * D * 2);
   const auto lrs = make_rsrc(a.lse + (size_t)bh * N, (uint32_t)N * 4);
   const auto drs = make_rsrc(a.delta + (size_t)bh * N, (uint32_t)N * 4);
 
@@ -207,8 +216,10 @@ __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs 
 
   const float c = a.c;  // never 0 (the host maps scale 0 to a tiny value)
   const float masked = c > 0.f ? -INFINITY : INFINITY;  // c * masked = -inf
-  const int q_begin = CAUSAL ? (k0 / C::BQ) * C::BQ : 0;
-  const int n_steps = (N - q_begin + C::BQ - 1) / C::BQ;  // >= 1 since k0 < N
+  // Causal: query i sees key j iff j <= i + qoff, so the first step that can see this tile holds
+  // query k0 - qoff; k0 < Nk = N + qoff keeps at least one step.
+  const int q_begin = CAUSAL ? (max(0, k0 - qoff) / C::BQ) * C::BQ : 0;
+  const int n_steps = (N - q_begin + C::BQ - 1) / C::BQ;
 
   // Block-sparse: the query steps (64 rows) whose 128-query block is live in this key tile's
   // column of the block mask (the key tile is exactly one 128-key block), compacted into a list
@@ -273,7 +284,7 @@ __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs 
 
   // Math of one query tile already staged in LDS stage `stage`.
   auto step_math = [&](int stage, int i0) {
-    const bool live = (i0 < N) && (!CAUSAL || (i0 + C::BQ - 1 >= kw0));
+    const bool live = (i0 < N) && (!CAUSAL || (i0 + C::BQ - 1 + qoff >= kw0));
     if (!live) return;
     const uint16_t* qs = smem + stage * C::STAGE;
     const uint16_t* os = qs + C::TILE;
@@ -300,15 +311,15 @@ __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs 
         pacc[qb] = mfma32x32x16<false>(da, vf[ks], pacc[qb]);
       }
     }
-    // Mask (keys beyond N; causal: key after query) on the few tiles that need it, as a score of
-    // -inf after scaling. Slot i holds query i0 + 32*qb + 16*(i/8) + 8*g + i%8.
-    if ((k0 + C::BKV > N) || (CAUSAL && (i0 < kw0 + 31))) {
+    // Mask (keys beyond Nk; causal: key after query + qoff) on the few tiles that need it, as a
+    // score of -inf after scaling. Slot i holds query i0 + 32*qb + 16*(i/8) + 8*g + i%8.
+    if ((k0 + C::BKV > Nk) || (CAUSAL && (i0 + qoff < kw0 + 31))) {
 #pragma unroll
       for (int qb = 0; qb < C::QBS; ++qb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int q = i0 + qb * 32 + (i >> 3) * 16 + g * 8 + (i & 7);
-          const bool dead = (key >= N) || (CAUSAL && key > q);
+          const bool dead = (key >= Nk) || (CAUSAL && key > q + qoff);
           sacc[qb][i] = dead ? masked : sacc[qb][i];
         }
     }
@@ -411,12 +422,12 @@ __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs 
 
   // Epilogue: dK = scale * (dK^T acc), dV = dV^T acc; accumulator rows are d, the column is
   // this lane's key.
-  if (key < N) {
+  if (key < Nk) {
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
-        const size_t off = head_off + (size_t)key * D + db * 32 + blk * 8 + g * 4;
+        const size_t off = kv_off + (size_t)key * D + db * 32 + blk * 8 + g * 4;
         store_grad4<G_F32, IS_BF16>(a.dk, off, dkacc[db][blk * 4] * a.scale,
                                     dkacc[db][blk * 4 + 1] * a.scale,
                                     dkacc[db][blk * 4 + 2] * a.scale,
@@ -456,16 +467,18 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
   const int g = lane >> 5;
   const int r = lane & 31;
-  const int N = a.N;
+  const int N = a.N;    // query rows
+  const int Nk = a.Nk;  // keys
+  const int qoff = a.qoff;
 
   int bh, tile;
   map_bwd_block(blockIdx.x, a.bh, CAUSAL, a.n_tiles, bh, tile);
-  const size_t head_off = (size_t)bh * N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const auto qrs = make_rsrc(a.q16 + head_off, head_bytes);
-  const auto krs = make_rsrc(a.k16 + head_off, head_bytes);
-  const auto vrs = make_rsrc(a.v16 + head_off, head_bytes);
-  const auto dors = make_rsrc(a.do16 + head_off, head_bytes);
+  const size_t q_off = (size_t)bh * N * D;
+  const size_t kv_off = (size_t)bh * Nk * D;
+  const auto qrs = make_rsrc(a.q16 + q_off, (uint32_t)N * D * 2);
+  const auto krs = make_rsrc(a.k16 + kv_off, (uint32_t)Nk * D * 2);
+  const auto vrs = make_rsrc(a.v16 + kv_off, (uint32_t)Nk * D * 2);
+  const auto dors = make_rsrc(a.do16 + q_off, (uint32_t)N * D * 2);
   const auto lrs = make_rsrc(a.lse + (size_t)bh * N, (uint32_t)N * 4);
   const auto drs = make_rsrc(a.delta + (size_t)bh * N, (uint32_t)N * 4);
 
@@ -493,7 +506,7 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
 
   const float c = a.c;  // never 0 (the host maps scale 0 to a tiny value)
   const float masked = c > 0.f ? -INFINITY : INFINITY;  // c * masked = -inf
-  const int kv_end = CAUSAL ? min(N, qt0 + C::BR) : N;
+  const int kv_end = CAUSAL ? min(Nk, qt0 + qoff + C::BR) : Nk;
   const int n_kt = (kv_end + C::BC - 1) / C::BC;
 
   // Block-sparse: live K/V tiles of this query tile's row of the block mask (as in the forward).
@@ -545,7 +558,7 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
   __syncthreads();
 
   auto tile_math = [&](int stage, int j0) {
-    const bool live = (j0 < kv_end) && (!CAUSAL || (j0 <= qw0 + 31));
+    const bool live = (j0 < kv_end) && (!CAUSAL || (j0 <= qw0 + qoff + 31));
     if (!live) return;
     const uint16_t* ks_ = smem + stage * C::STAGE;
     const uint16_t* vs_ = ks_ + C::TILE;
@@ -571,13 +584,13 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
     }
     // Mask on the few tiles that need it. Slot i of block kb holds key
     // j0 + 32*kb + 16*(i/8) + 8*g + i%8.
-    if ((j0 + C::BC > N) || (CAUSAL && (j0 + C::BC - 1 > qw0))) {
+    if ((j0 + C::BC > Nk) || (CAUSAL && (j0 + C::BC - 1 > qw0 + qoff))) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int kk = j0 + kb * 32 + (i >> 3) * 16 + g * 8 + (i & 7);
-          const bool dead = (kk >= N) || (CAUSAL && kk > qrow);
+          const bool dead = (kk >= Nk) || (CAUSAL && kk > qrow + qoff);
           sacc[kb][i] = dead ? masked : sacc[kb][i];
         }
     }
@@ -642,7 +655,7 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
-        const size_t off = head_off + (size_t)qrow * D + db * 32 + blk * 8 + g * 4;
+        const size_t off = q_off + (size_t)qrow * D + db * 32 + blk * 8 + g * 4;
         store_grad4<G_F32, IS_BF16>(a.dq, off, dqacc[db][blk * 4] * a.scale,
                                     dqacc[db][blk * 4 + 1] * a.scale,
                                     dqacc[db][blk * 4 + 2] * a.scale,
@@ -656,13 +669,17 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
 // ----------------------------------------------------------------------------------------
 template <int D, bool IS_BF16>
 static hipError_t launch_pre(const BwdArgs& a, bool o_f32, hipStream_t s) {
-  const long long rows = (long long)a.bh * a.N;
+  const long long rows_q = (long long)a.bh * a.N;
+  const long long rows_k = (long long)a.bh * a.Nk;
+  const long long rows = rows_q > rows_k ? rows_q : rows_k;
   constexpr int RPB = 256 / pre_tpr<D>();
   const int grid = (int)((rows + RPB - 1) / RPB);
   if (o_f32)
-    hipLaunchKernelGGL((bwd_pre_kernel<D, IS_BF16, true>), dim3(grid), dim3(256), 0, s, a, rows);
+    hipLaunchKernelGGL((bwd_pre_kernel<D, IS_BF16, true>), dim3(grid), dim3(256), 0, s, a, rows_q,
+                       rows_k);
   else
-    hipLaunchKernelGGL((bwd_pre_kernel<D, IS_BF16, false>), dim3(grid), dim3(256), 0, s, a, rows);
+    hipLaunchKernelGGL((bwd_pre_kernel<D, IS_BF16, false>), dim3(grid), dim3(256), 0, s, a, rows_q,
+                       rows_k);
   return hipGetLastError();
 }
 
@@ -680,7 +697,7 @@ static hipError_t launch_grads(BwdArgs a, hipStream_t s, hipEvent_t ev_before,
                                hipEvent_t ev_after) {
   hipError_t e;
   if (ev_before && (e = hipEventRecord(ev_before, s)) != hipSuccess) return e;
-  a.n_tiles = (a.N + Dkdv<D>::BKV - 1) / Dkdv<D>::BKV;
+  a.n_tiles = (a.Nk + Dkdv<D>::BKV - 1) / Dkdv<D>::BKV;
   e = launch_dyn(bwd_dkdv_kernel<D, IS_BF16, G_F32, CAUSAL, DROP, SPARSE>, a.n_tiles * a.bh,
                  Dkdv<D>::LDS_BYTES + (DROP ? Dkdv<D>::MASK_BYTES : 0) +
                      (SPARSE ? kSparseListBytes : 0),

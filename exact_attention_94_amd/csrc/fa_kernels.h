@@ -45,14 +45,19 @@ struct BwdArgs {
   void* dv;
   float* delta;  // float32 [B,H,N]: rowsum(dO * O)
   // fp16 operands of the gradient kernels: the inputs themselves for fp16 inputs; for bf16
-  // inputs, the copies the preprocess kernel writes to ws16 (Q, K, V, dO, `elems` apart).
+  // inputs, the copies the preprocess kernel writes into the workspace (ws_q .. ws_do, which
+  // are null for fp16 inputs).
   const uint16_t* q16;
   const uint16_t* k16;
   const uint16_t* v16;
   const uint16_t* do16;
-  uint16_t* ws16;
-  size_t elems;  // B*H*N*d
-  int N;
+  uint16_t* ws_q;
+  uint16_t* ws_k;
+  uint16_t* ws_v;
+  uint16_t* ws_do;
+  int N;     // query rows per head
+  int Nk;    // keys per head (= N for self-attention)
+  int qoff;  // position of query row 0 in the key sequence (causal alignment), usually 0
   int bh;
   int n_tiles;
   float scale;

@@ -118,6 +118,27 @@ fa_status fa_backward(const void* q, const void* k, const void* v, const void* o
                       size_t workspace_bytes, void* stream);
 
 /*
+ * Bytes of device workspace fa_backward_kv needs: D (float32 [B,H,Nq]) and, when in_dtype is
+ * FA_BF16, fp16 copies of Q and dO ([B,H,Nq,d] each) and of K and V ([B,H,Nk,d] each). Equal to
+ * fa_backward_workspace_bytes when Nq = Nk. Returns 0 for arguments fa_backward_kv would reject.
+ */
+size_t fa_backward_kv_workspace_bytes(int B, int H, int Nq, int Nk, int d, fa_dtype in_dtype,
+                                      fa_dtype grad_dtype);
+
+/*
+ * Backward pass of fa_forward_kv (same gradients as fa_backward, over Nq queries and Nk keys):
+ *   q, o, dout, dq  [B,H,Nq,d];  k, v, dk, dv [B,H,Nk,d];  lse [B,H,Nq]
+ *   causal          as in fa_forward_kv (queries are the last Nq positions; Nq <= Nk)
+ *   workspace       at least fa_backward_kv_workspace_bytes(B,H,Nq,Nk,d,in_dtype,grad_dtype)
+ * Keys that no query sees get dK = dV = 0. Dtypes, workspace rules and errors as fa_backward.
+ */
+fa_status fa_backward_kv(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                         int H, int Nq, int Nk, int d, float scale, int causal,
+                         fa_dtype in_dtype, fa_dtype o_dtype, fa_dtype grad_dtype,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Forward pass with dropout on the attention probabilities ("FlashAttention 为什么不需要存下注意力矩阵"
  * §05, fourth difference: the kernel keeps no mask, only the random generator's seed and
  * offset, and the backward pass regenerates the same mask from them).

@@ -249,6 +249,54 @@ def test_forward_kv_rejects(kw, status):
     assert fwd_kv(**kw) == status
 
 
+def bwd_kv(**kw):
+    a = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=2, H=3, Nq=100, Nk=300, d=64,
+             scale=0.125, causal=1, in_dtype=B.FA_BF16, o_dtype=B.FA_F32, g_dtype=B.FA_F32,
+             ws=P, ws_bytes=1 << 30)
+    a.update(kw)
+    return _lib().fa_backward_kv(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"],
+                                 a["dk"], a["dv"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"],
+                                 a["scale"], a["causal"], a["in_dtype"], a["o_dtype"],
+                                 a["g_dtype"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Nq=301), B.FA_ERR_INVALID_ARG),          # causal needs Nq <= Nk
+    (dict(Nk=0), B.FA_ERR_INVALID_ARG),
+    (dict(Nq=0), B.FA_ERR_INVALID_ARG),
+    (dict(dk=None), B.FA_ERR_INVALID_ARG),
+    (dict(dv=P + 4), B.FA_ERR_INVALID_ARG),
+    (dict(in_dtype=B.FA_F32, o_dtype=B.FA_F32), B.FA_ERR_UNSUPPORTED),
+    (dict(d=256), B.FA_ERR_UNSUPPORTED),
+    (dict(d=80), B.FA_ERR_UNSUPPORTED),
+    (dict(B=1, H=1, Nk=(1 << 24) + 1), B.FA_ERR_INVALID_ARG),
+    (dict(ws=None), B.FA_ERR_WORKSPACE),
+    # Q / dO copies over Nq rows, K / V copies over Nk rows: one byte short is rejected.
+    (dict(ws_bytes=2560 + (2 * 2 * 3 * 100 * 64 + 2 * 2 * 3 * 300 * 64) * 2 - 1),
+     B.FA_ERR_WORKSPACE),
+])
+def test_backward_kv_rejects(kw, status):
+    assert bwd_kv(**kw) == status
+
+
+def test_backward_kv_workspace_bytes():
+    lib = _lib()
+    ws = lib.fa_backward_kv_workspace_bytes
+    assert ws(2, 3, 100, 300, 64, B.FA_F16, B.FA_F32) == 2560
+    assert ws(2, 3, 100, 300, 64, B.FA_BF16, B.FA_F32) == \
+        2560 + (2 * 2 * 3 * 100 * 64 + 2 * 2 * 3 * 300 * 64) * 2
+    # Non-causal calls may have more queries than keys.
+    assert ws(1, 1, 300, 17, 32, B.FA_BF16, B.FA_BF16) == \
+        round(300 * 4 / 256 + 0.5) * 256 + (2 * 300 * 32 + 2 * 17 * 32) * 2
+    for n in (1, 100, 4099):
+        for dt in (B.FA_F16, B.FA_BF16):
+            assert ws(2, 3, n, n, 96, dt, B.FA_F32) == \
+                lib.fa_backward_workspace_bytes(2, 3, n, 96, dt, B.FA_F32)
+    assert ws(1, 1, 10, 10, 256, B.FA_F16, B.FA_F32) == 0
+    assert ws(1, 1, 10, 0, 64, B.FA_F16, B.FA_F32) == 0
+    assert ws(1, 1, 10, 10, 64, B.FA_F16, 9) == 0
+
+
 def test_workspace_bytes():
     lib = _lib()
     ws = lib.fa_backward_workspace_bytes
