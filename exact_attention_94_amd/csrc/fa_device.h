@@ -94,20 +94,25 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 
 // Swizzled tile layout (rows of D 16-bit elements, no padding): logical 16-byte chunk c of row r
-// is stored at chunk c ^ swz<D>(r), with the 128-byte window of 32 four-byte banks in mind.
-//  * D a multiple of 64 (rows a multiple of 128 bytes, so every row starts on bank 0): swz is a
-//    bijection of r mod 8 onto 0..7, so the eight rows an MFMA operand read (ds_read_b128)
-//    touches at one chunk land on eight different chunks; and it puts two of every four
-//    consecutive rows in each half of the window, which balances the transposed reads
-//    (ds_read_b64_tr_b16: four rows x 64 bytes per 16 lanes).
-//  * D = 32 or 96 (rows start alternately on bank 0 and bank 16): even and odd rows already fall
-//    in different halves, and swz = (r / 2) mod 4 separates the four even (odd) rows of a
-//    ds_read_b128. It only permutes chunks within aligned groups of four, which the transposed
-//    reads (64 bytes = one aligned group per row) leave intact.
+// is stored at chunk c ^ swz<D>(r). gfx950's LDS has 64 four-byte banks (a 256-byte window); a
+// ds_read_b128 is served 16 lanes at a time and a ds_read_b64_tr_b16 32 lanes at a time. The two
+// read patterns used on these tiles are:
+//   (A) MFMA operand rows: 16 consecutive rows (aligned), one logical chunk each;
+//   (B) transposed operand reads: 4 consecutive rows (aligned) x 4 consecutive chunks (aligned).
+// swz makes both hit 16 distinct 16-byte bank slots:
+//  * D = 64 (two rows per window): (A) needs a bijection of (r / 2) mod 8 for each row parity;
+//    (B) needs rows r and r + 2 to differ in bit 2 (they share a window half). Both hold for
+//    swz = 4 ((r / 2) mod 2) + (r / 4) mod 4.
+//  * D = 128 or 256 (rows a multiple of the window): (A) needs a bijection of r mod 16; (B) needs
+//    bits 2..3 to differ between 4 consecutive rows. swz = 4 (r mod 4) + (r / 4) mod 4.
+//  * D = 32 or 96 (row starts step through the window by 64 bytes): (A) needs the four rows with
+//    the same r mod 4 to differ, swz = (r / 4) mod 4, which only permutes chunks within aligned
+//    groups of four; (B) is conflict-free for any such permutation.
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-  if constexpr (D % 64 == 0) return ((row & 1) << 2) | ((row >> 1) & 3);
-  return (row >> 1) & 3;
+  if constexpr (D == 64) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  if constexpr (D % 128 == 0) return ((row & 3) << 2) | ((row >> 2) & 3);
+  return (row >> 2) & 3;
 }
 template <int D>
 __device__ __forceinline__ int swz_off(int row, int col) {

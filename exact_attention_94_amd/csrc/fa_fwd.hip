@@ -27,7 +27,10 @@
 //     registers, no LDS write instructions. Tile rows are unpadded and swizzled (swz_off), which
 //     keeps both the row reads of K and the transposed reads of V free of bank conflicts;
 //   * workgroups are ordered longest-first for causal masks and grouped per XCD so that the
-//     query tiles of one (b, h) share an L2.
+//     query tiles of one (b, h) share an L2;
+//   * plain attention at d <= 128 runs fwd16pp_kernel: two groups of four waves that alternate
+//     a softmax phase and an MFMA phase, one phase apart, so that each SIMD always holds one wave
+//     of each kind. Dropout, block-sparse masks and d = 256 run fwd16_kernel (one group).
 #include "fa_device.h"
 #include "fa_kernels.h"
 #include "fa_tune.h"
@@ -385,6 +388,285 @@ __global__ __launch_bounds__(256, fwd_min_waves<D>()) void fwd16_kernel(FwdArgs 
 }
 
 // ----------------------------------------------------------------------------------------
+// Two-group variant for plain attention: 8 waves (256 queries, 32 per wave) per workgroup in two
+// groups of four; waves w and w + 4 share a SIMD. Each wave alternates two phases per K/V tile:
+//   V phase (vector ALU): mask, online softmax of its score tile S_t -> P_t, rescale of O;
+//   M phase (matrix cores + LDS): O += V_t P_t, then S_{t+1} = K_{t+1} Q^T.
+// Group 1 runs one phase behind group 0 and every phase ends with a workgroup barrier, so on each
+// SIMD one wave is in its M phase while the other is in its V phase: the exp / FMA stream of one
+// wave issues alongside the MFMA stream of the other.
+// LDS holds two K and two V stages (tile t in stage t mod 2). With phase 2t the V phase of group
+// 0 for tile t (and the M phase of group 1 for tile t-1):
+//   K_t is read in phases 2t-1 and 2t; V_t in phases 2t+1 and 2t+2;
+//   group 0 issues K_{t+1} in phase 2t (its stage last held K_{t-1}, read up to phase 2t-2) and
+//   waits for it at the end of that phase; group 1 issues V_{t+1} in phase 2t+1 (stage of
+//   V_{t-1}, read up to phase 2t) and waits for it at the end of phase 2t+2.
+// ----------------------------------------------------------------------------------------
+template <int D>
+struct FwdPP {
+  static constexpr int NW = 8;
+  static constexpr int NT = NW * 64;
+  static constexpr int BR = NW * 32;
+  static constexpr int BC = fwd_tile_keys<D>();
+  static constexpr int KB = BC / 32;
+  static constexpr int KS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int KTILE = BC * D;
+  static constexpr int LD_INSTR = BC * D * 2 / 1024;  // 1 KB direct loads per tile and tensor
+  static constexpr int LPW = LD_INSTR / 4;            // per wave of one group
+  static constexpr int LDS_BYTES = 4 * KTILE * 2;
+  static_assert(LD_INSTR % 4 == 0, "each wave of a group issues whole 1 KB loads");
+};
+
+// Workgroup barrier without a memory fence: no wait on this wave's outstanding direct loads.
+// The empty asm statements keep the compiler from moving LDS accesses across it, and the
+// scheduling barriers keep every other instruction on its side, so the phases stay phases.
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int D, bool IS_BF16, bool O_F32, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void fwd16pp_kernel(FwdArgs a) {
+  using C = FwdPP<D>;
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int wg = wave & 3;  // index within the group
+  const int g = lane >> 5;
+  const int r = lane & 31;
+  const int N = a.N;
+  const int Nk = a.Nk;
+  const int qoff = a.qoff;
+
+  int bh, tile;
+  map_block(blockIdx.x, a.n_tiles, a.bh, CAUSAL, bh, tile);
+  const size_t head_off = (size_t)bh * N * D;
+  const size_t kv_off = (size_t)bh * Nk * D;
+  const auto qrs = make_rsrc(static_cast<const uint16_t*>(a.q) + head_off, (uint32_t)N * D * 2);
+  const auto krs = make_rsrc(static_cast<const uint16_t*>(a.k) + kv_off, (uint32_t)Nk * D * 2);
+  const auto vrs = make_rsrc(static_cast<const uint16_t*>(a.v) + kv_off, (uint32_t)Nk * D * 2);
+
+  const int qt0 = tile * C::BR;
+  const int qw0 = qt0 + wave * 32;
+
+  const uint32_t qsign = a.c < 0.f ? 0x80008000u : 0u;
+  Frag16 qf[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    qf[ks].w = buf_ld16(qrs, (uint32_t)((qw0 + r) * D + ks * 16 + g * 8) * 2);
+    qf[ks].w ^= qsign;
+  }
+
+  f32x16 oacc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  float m_run = -3.0e38f, l_run = 0.f;
+  const float c = __builtin_fabsf(a.c);
+
+  const int kv_end = CAUSAL ? min(Nk, qt0 + qoff + C::BR) : Nk;
+  const int n_kt = (kv_end + C::BC - 1) / C::BC;
+
+  uint16_t* const k_st = smem;
+  uint16_t* const v_st = smem + 2 * C::KTILE;
+
+  // Direct loads of one tile by the four waves of a group (group 0 loads K, group 1 V): wave wg
+  // issues 1 KB loads t = wg, wg + 4, ...; lane l of load t fills element 512 t + 8 l of the tile
+  // (swizzled rows; K rows in key_of_krow order).
+  uint32_t loff[C::LPW];
+#pragma unroll
+  for (int i = 0; i < C::LPW; ++i) {
+    const int e = (wg + i * 4) * 512 + lane * 8;
+    const int R = e / D, pch = (e % D) >> 3;
+    const int cch = pch ^ swz<D>(R);
+    const int key = grp == 0 ? (R & ~31) + key_of_krow(R & 31) : R;
+    loff[i] = (uint32_t)(key * D + cch * 8) * 2;
+  }
+  auto load_k = [&](int stage, int t) {
+    uint16_t* dst = k_st + stage * C::KTILE;
+    const uint32_t base = (uint32_t)(t * C::BC) * D * 2;
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i) buf_ld16_lds(krs, base + loff[i], dst + (wg + i * 4) * 512);
+  };
+  auto load_v = [&](int stage, int t) {
+    uint16_t* dst = v_st + stage * C::KTILE;
+    const uint32_t base = (uint32_t)(t * C::BC) * D * 2;
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i) buf_ld16_lds(vrs, base + loff[i], dst + (wg + i * 4) * 512);
+  };
+
+  // Every wave processes every tile of the workgroup: a tile entirely after a wave's queries is
+  // masked to -inf, which leaves m, l and O exactly unchanged (tile 0 is never of that kind, so
+  // m is finite from the first tile on). This costs at most one tile per wave and keeps the
+  // phases branch-free.
+  f32x16 s[C::KB];
+  Frag16 pf[C::KB][2];
+
+  // M phase of tile t: O += V_t P_t (V stage t % 2), then S_{t+1} (K stage (t + 1) % 2).
+  auto m_phase = [&](int t, int vstage, int kstage) {
+    if (t >= 0) {
+      const uint16_t* vs_ = v_st + vstage * C::KTILE;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int row = kb * 32 + h * 16 + g * 8;
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) {
+            Frag16 vf;
+            vf.w = lds_tr_frag_swz<D>(vs_, row, row + 4, db * 32);
+            oacc[db] = mfma32x32x16<IS_BF16>(vf, pf[kb][h], oacc[db]);
+          }
+        }
+    }
+    if (t + 1 < n_kt) {
+      const uint16_t* ks_ = k_st + kstage * C::KTILE;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) {
+          Frag16 kf;
+          kf.w = *reinterpret_cast<const u32x4*>(ks_ + swz_off<D>(kb * 32 + r, ks * 16 + g * 8));
+          s[kb] = mfma32x32x16<IS_BF16>(kf, qf[ks], s[kb]);
+        }
+    }
+  };
+
+  // V phase of tile t: mask, online softmax, rescale.
+  auto v_phase = [&](int t) {
+    const int j0 = t * C::BC;
+    if ((j0 + C::BC > Nk) || (CAUSAL && (j0 + C::BC - 1 > qw0 + qoff))) {
+      // Slot i of block kb holds key j0 + g*8 + ci, ci = 32kb + 16(i/8) + i%8 (a constant); the
+      // key is dead past Nk - 1 and, when causal, past this lane's query position. One bound per
+      // tile keeps the comparisons against immediates.
+      int bound = Nk - 1 - j0 - g * 8;
+      if (CAUSAL) bound = min(bound, qw0 + r + qoff - j0 - g * 8);
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ci = kb * 32 + (i >> 3) * 16 + (i & 7);
+          s[kb][i] = ci > bound ? -INFINITY : s[kb][i];
+        }
+    }
+    float red = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) red = __builtin_fmaxf(red, s[kb][i]);
+    red = halves_max(red);
+    const float m_new = __builtin_fmaxf(m_run, red * c);
+    const float corr = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    l_run *= corr;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] *= corr;
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = fast_exp2(__builtin_fmaf(s[kb][h * 8 + e], c, -m_new));
+          lsum += p[e];
+        }
+        pf[kb][h].w = u32x4{pack2<IS_BF16>(p[0], p[1]), pack2<IS_BF16>(p[2], p[3]),
+                            pack2<IS_BF16>(p[4], p[5]), pack2<IS_BF16>(p[6], p[7])};
+      }
+    l_run += lsum;
+  };
+
+  // Prologue: K_0 (group 0) and V_0 (group 1); then group 0 computes S_0.
+  if (grp == 0) load_k(0, 0);
+  else load_v(0, 0);
+  wait_vmem_all();
+  __syncthreads();
+
+  if (grp == 0) {
+    m_phase(-1, 1, 0);
+    wg_barrier();
+    for (int t = 0; t < n_kt; t += 2) {
+      load_k(1, t + 1);
+      v_phase(t);
+      wait_vmem_all();
+      wg_barrier();
+      m_phase(t, 0, 1);
+      wg_barrier();
+      if (t + 1 >= n_kt) break;
+      load_k(0, t + 2);
+      v_phase(t + 1);
+      wait_vmem_all();
+      wg_barrier();
+      m_phase(t + 1, 1, 0);
+      wg_barrier();
+    }
+  } else {
+    wg_barrier();
+    for (int t = 0; t < n_kt; t += 2) {
+      m_phase(t - 1, 1, 0);
+      wait_vmem_all();
+      wg_barrier();
+      load_v(1, t + 1);
+      v_phase(t);
+      wg_barrier();
+      if (t + 1 >= n_kt) break;
+      m_phase(t, 0, 1);
+      wait_vmem_all();
+      wg_barrier();
+      load_v(0, t + 2);
+      v_phase(t + 1);
+      wg_barrier();
+    }
+    // P.V of the last tile (its V stage is not the target of the load still in flight).
+    if (n_kt & 1) m_phase(n_kt - 1, 0, 1);
+    else m_phase(n_kt - 1, 1, 0);
+    wait_vmem_all();
+  }
+
+// Epilogue: O / l, LSE = (m + log2 l) * ln 2.
+  const int qrow = qw0 + r;
+  const float l_tot = halves_sum(l_run);
+  const float inv = 1.f / l_tot;
+  if (qrow < N) {
+    if (g == 0) a.lse[(size_t)bh * N + qrow] = (m_run + fast_log2(l_tot)) * kLn2;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const int d0 = db * 32 + blk * 8 + g * 4;
+        const float o0 = oacc[db][blk * 4 + 0] * inv;
+        const float o1 = oacc[db][blk * 4 + 1] * inv;
+        const float o2 = oacc[db][blk * 4 + 2] * inv;
+        const float o3 = oacc[db][blk * 4 + 3] * inv;
+        if constexpr (O_F32) {
+          float* dst = static_cast<float*>(a.o) + head_off + (size_t)qrow * D + d0;
+          *reinterpret_cast<f32x4*>(dst) = f32x4{o0, o1, o2, o3};
+        } else {
+          uint16_t* dst = static_cast<uint16_t*>(a.o) + head_off + (size_t)qrow * D + d0;
+          *reinterpret_cast<u32x2*>(dst) = u32x2{pack2<IS_BF16>(o0, o1), pack2<IS_BF16>(o2, o3)};
+        }
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------------------
 // fp32 inputs: the same recurrence on true-fp32 MFMA (v_mfma_f32_32x32x2_f32). One wave owns
 // 32 queries, K/V tiles of 32 keys are staged in LDS in natural [key][d] layout (one float per
 // lane per operand, so no transposition is needed).
@@ -535,9 +817,28 @@ static hipError_t launch16(FwdArgs a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D, bool IS_BF16, bool O_F32, bool CAUSAL>
+static hipError_t launch16pp(FwdArgs a, hipStream_t s) {
+  using C = FwdPP<D>;
+  a.n_tiles = (a.N + C::BR - 1) / C::BR;
+  const int grid = a.n_tiles * a.bh;
+  constexpr int lds = C::LDS_BYTES;
+  auto kern = fwd16pp_kernel<D, IS_BF16, O_F32, CAUSAL>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), lds, s, a);
+  return hipGetLastError();
+}
+
+// Plain attention at d <= 128 runs the two-group kernel; dropout, block-sparse masks and d = 256
+// the single-group one.
 template <int D, bool IS_BF16, bool O_F32, bool DROP, bool SPARSE>
 static hipError_t launch16_m(FwdArgs a, bool causal, hipStream_t s) {
   constexpr int QB = fwd_qb<D>();
+  if constexpr (!DROP && !SPARSE && D <= 128)
+    return causal ? launch16pp<D, IS_BF16, O_F32, true>(a, s)
+                  : launch16pp<D, IS_BF16, O_F32, false>(a, s);
   return causal ? launch16<D, IS_BF16, O_F32, true, QB, DROP, SPARSE>(a, s)
                 : launch16<D, IS_BF16, O_F32, false, QB, DROP, SPARSE>(a, s);
 }
