@@ -30,6 +30,7 @@
 // issued one step ahead, into unpadded rows with the chunk swizzle of swz_off.
 #include "fa_device.h"
 #include "fa_kernels.h"
+#include "fa_tune.h"
 
 namespace fa {
 
@@ -300,17 +301,18 @@ __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs 
         sacc[qb][i] = 0.f;
         pacc[qb][i] = 0.f;
       }
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-#pragma unroll
-      for (int qb = 0; qb < C::QBS; ++qb) {
-        Frag16 qa, da;
-        qa.w = *reinterpret_cast<const u32x4*>(qs + swz_off<D>(qb * 32 + r, ks * 16 + g * 8));
-        da.w = *reinterpret_cast<const u32x4*>(os + swz_off<D>(qb * 32 + r, ks * 16 + g * 8));
-        sacc[qb] = mfma32x32x16<false>(qa, kf[ks], sacc[qb]);
-        pacc[qb] = mfma32x32x16<false>(da, vf[ks], pacc[qb]);
-      }
-    }
+    // Fragment f = (ks, qb, tensor: Q for S, dO for dP), read dkdv_pre<D>() ahead of its MFMA.
+    read_ahead<2 * C::KS * C::QBS, dkdv_pre<D>()>(
+        [&](int f) {
+          const int ks = f / (2 * C::QBS), qb = (f / 2) % C::QBS;
+          const uint16_t* src = (f & 1) ? os : qs;
+          return *reinterpret_cast<const u32x4*>(src + swz_off<D>(qb * 32 + r, ks * 16 + g * 8));
+        },
+        [&](int f, const Frag16& fr) {
+          const int ks = f / (2 * C::QBS), qb = (f / 2) % C::QBS;
+          if (f & 1) pacc[qb] = mfma32x32x16<false>(fr, vf[ks], pacc[qb]);
+          else sacc[qb] = mfma32x32x16<false>(fr, kf[ks], sacc[qb]);
+        });
     // Mask (keys beyond Nk; causal: key after query + qoff) on the few tiles that need it, as a
     // score of -inf after scaling. Slot i holds query i0 + 32*qb + 16*(i/8) + 8*g + i%8.
     if ((k0 + C::BKV > Nk) || (CAUSAL && (i0 + qoff < kw0 + 31))) {
@@ -454,7 +456,7 @@ struct Dq {
   static constexpr int STAGE = 2 * TILE;  // K then V
   static constexpr int LDS_BYTES = 2 * STAGE * 2;
   static constexpr int LD_INSTR = BC * D * 2 / 1024;  // 1 KB direct loads per tile and tensor
-  static constexpr int MIN_WG = (D <= 64) ? 3 : 2;
+  static constexpr int MIN_WG = (D <= 64) ? kDqWaves64 : 2;
 };
 
 template <int D, bool IS_BF16, bool G_F32, bool CAUSAL, bool DROP, bool SPARSE>
@@ -571,17 +573,18 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
         sacc[kb][i] = 0.f;
         pacc[kb][i] = 0.f;
       }
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        Frag16 ka, va;
-        ka.w = *reinterpret_cast<const u32x4*>(ks_ + swz_off<D>(kb * 32 + r, ks * 16 + g * 8));
-        va.w = *reinterpret_cast<const u32x4*>(vs_ + swz_off<D>(kb * 32 + r, ks * 16 + g * 8));
-        sacc[kb] = mfma32x32x16<false>(ka, qf[ks], sacc[kb]);
-        pacc[kb] = mfma32x32x16<false>(va, of[ks], pacc[kb]);
-      }
-    }
+    // Fragment f = (ks, kb, tensor: K for S^T, V for dP^T), read dq_pre<D>() ahead of its MFMA.
+    read_ahead<2 * C::KS * 2, dq_pre<D>()>(
+        [&](int f) {
+          const int ks = f / 4, kb = (f / 2) % 2;
+          const uint16_t* src = (f & 1) ? vs_ : ks_;
+          return *reinterpret_cast<const u32x4*>(src + swz_off<D>(kb * 32 + r, ks * 16 + g * 8));
+        },
+        [&](int f, const Frag16& fr) {
+          const int ks = f / 4, kb = (f / 2) % 2;
+          if (f & 1) pacc[kb] = mfma32x32x16<false>(fr, of[ks], pacc[kb]);
+          else sacc[kb] = mfma32x32x16<false>(fr, qf[ks], sacc[kb]);
+        });
     // Mask on the few tiles that need it. Slot i of block kb holds key
     // j0 + 32*kb + 16*(i/8) + 8*g + i%8.
     if ((j0 + C::BC > Nk) || (CAUSAL && (j0 + C::BC - 1 > qw0 + qoff))) {

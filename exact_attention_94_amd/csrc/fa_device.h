@@ -174,6 +174,37 @@ __device__ __forceinline__ float buf_ldf(__amdgpu_buffer_rsrc_t r, uint32_t byte
 // for the loop's own prefetches.
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// A run of NF MFMAs whose operands come from LDS, fragment f read by read(f) (returning the
+// 16 bytes) and consumed by use(f, frag) in that order, with the read of fragment f + PRE
+// issued before the MFMA of fragment f. The scheduling barrier after each step keeps that
+// order: left alone, the scheduler sinks each read to just ahead of its use to save registers,
+// so that every MFMA waits out the LDS latency. Only the order of independent instructions
+// changes; the arithmetic is the same.
+// PRE = 0 leaves the order to the scheduler.
+template <int NF, int PRE, typename Read, typename Use>
+__device__ __forceinline__ void read_ahead(Read&& read, Use&& use) {
+  static_assert(PRE >= 0, "prefetch depth out of range");
+  if constexpr (PRE == 0) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      Frag16 fr;
+      fr.w = read(f);
+      use(f, fr);
+    }
+    return;
+  }
+  constexpr int P = PRE < NF ? PRE : NF;
+  Frag16 fr[NF];
+#pragma unroll
+  for (int f = 0; f < P; ++f) fr[f].w = read(f);
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    if (f + P < NF) fr[f + P].w = read(f + P);
+    use(f, fr[f]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

@@ -533,14 +533,17 @@ __global__ __launch_bounds__(512, 1) void fwd16pp_kernel(FwdArgs a) {
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) {
-          Frag16 kf;
-          kf.w = *reinterpret_cast<const u32x4*>(ks_ + swz_off<D>(kb * 32 + r, ks * 16 + g * 8));
-          s[kb] = mfma32x32x16<IS_BF16>(kf, qf[ks], s[kb]);
-        }
+      // Fragment f = (ks, kb) of K, read fwd_pre<D>() fragments ahead of its MFMA.
+      read_ahead<C::KS * C::KB, fwd_pre<D>()>(
+          [&](int f) {
+            const int ks = f / C::KB, kb = f % C::KB;
+            return *reinterpret_cast<const u32x4*>(ks_ +
+                                                   swz_off<D>(kb * 32 + r, ks * 16 + g * 8));
+          },
+          [&](int f, const Frag16& kf) {
+            const int ks = f / C::KB, kb = f % C::KB;
+            s[kb] = mfma32x32x16<IS_BF16>(kf, qf[ks], s[kb]);
+          });
     }
   };
 
@@ -561,11 +564,15 @@ __global__ __launch_bounds__(512, 1) void fwd16pp_kernel(FwdArgs a) {
           s[kb][i] = ci > bound ? -INFINITY : s[kb][i];
         }
     }
-    float red = s[0][0];
+    // Row maximum as four independent chains (a single chain would serialise ~32 dependent
+    // max3 instructions while this wave is the only VALU issuer on its SIMD).
+    float red4[4] = {s[0][0], s[0][1], s[0][2], s[0][3]};
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) red = __builtin_fmaxf(red, s[kb][i]);
+      for (int i = 0; i < 16; ++i) red4[i & 3] = __builtin_fmaxf(red4[i & 3], s[kb][i]);
+    float red = __builtin_fmaxf(__builtin_fmaxf(red4[0], red4[1]),
+                                __builtin_fmaxf(red4[2], red4[3]));
     red = halves_max(red);
     const float m_new = __builtin_fmaxf(m_run, red * c);
     const float corr = fast_exp2(m_run - m_new);

@@ -25,7 +25,39 @@
 #define FA_FWD_BC_256 32
 #endif
 
+// LDS operand reads kept in flight ahead of the MFMAs of the score products (forward S, and S
+// with dP in both backward kernels); overridable with -DFA_FWD_PRE / -DFA_DKDV_PRE / -DFA_DQ_PRE.
+#ifndef FA_FWD_PRE
+#define FA_FWD_PRE 4
+#endif
+#ifndef FA_DKDV_PRE
+#define FA_DKDV_PRE 4
+#endif
+#ifndef FA_DQ_PRE
+#define FA_DQ_PRE 4
+#endif
+// Waves per SIMD the dQ kernel's register allocation must allow at d <= 64.
+#ifndef FA_DQ_WAVES_64
+#define FA_DQ_WAVES_64 2
+#endif
+
 namespace fa {
+
+// Measured at d = 64 only (dK/dV kernel 4% faster); other head dims keep the scheduler's own
+// order (at d = 128 the read-ahead makes the dQ kernel spill).
+template <int D>
+constexpr int fwd_pre() {
+  return D == 64 ? FA_FWD_PRE : 0;
+}
+template <int D>
+constexpr int dkdv_pre() {
+  return D == 64 ? FA_DKDV_PRE : 0;
+}
+template <int D>
+constexpr int dq_pre() {
+  return D == 64 ? FA_DQ_PRE : 0;
+}
+constexpr int kDqWaves64 = FA_DQ_WAVES_64;
 
 template <int D>
 constexpr int fwd_tile_keys() {
