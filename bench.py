@@ -44,7 +44,7 @@ METRIC = "attention fwd/bwd TFLOP/s + % bf16 MFMA peak (B2 H16 N4096 d64 causal)
 WORKLOAD = "b2h16n4k_d64"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_dkdv_b2h16n4k_d64_traffic.txt")
 KERNEL_SOURCES = tuple(os.path.join(ROOT, "exact_attention_94_amd", "csrc", f)
-                       for f in ("fa_bwd.hip", "fa_device.h", "fa_kernels.h"))
+                       for f in ("fa_bwd.hip", "fa_device.h", "fa_kernels.h", "fa_tune.h"))
 
 
 def flops(w):
