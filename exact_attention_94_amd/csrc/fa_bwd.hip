@@ -9,10 +9,12 @@
 //
 // Kernels (one stream, in order):
 //   1. bwd_pre:   D = rowsum(dO * O) in fp32 from the forward's output; for bf16 inputs, fp16
-//                 copies of Q, K, V, dO in the workspace.
+//                 copies of Q and dO in the workspace.
 //   2. bwd_dkdv:  keys outer. One workgroup per tile of 128 keys (4 waves x 32 keys) keeps dK and
 //                 dV in registers over all query tiles (causal: those at or below the
-//                 diagonal): S, dP, then P, dS, then dV += P^T dO and dK += dS^T Q.
+//                 diagonal): S, dP, then P, dS, then dV += P^T dO and dK += dS^T Q. For bf16
+//                 inputs it converts its own K and V rows to fp16 on load and writes them to the
+//                 workspace for the dQ kernel.
 //   3. bwd_dq:    queries outer, like the forward. One workgroup per tile of 128 queries keeps
 //                 dQ in registers over all key tiles: S^T, dP^T, then dS^T, then
 //                 dQ^T += K^T dS^T; dQ is written once, in the output dtype.
@@ -35,7 +37,7 @@
 namespace fa {
 
 // ----------------------------------------------------------------------------------------
-// 1. D = rowsum(dO * O); for bf16 inputs, fp16 copies of Q, K, V and dO.
+// 1. D = rowsum(dO * O); for bf16 inputs, fp16 copies of Q and dO.
 // ----------------------------------------------------------------------------------------
 template <bool IS_BF16>
 __device__ __forceinline__ u32x4 to_f16x8(u32x4 v) {
@@ -57,11 +59,10 @@ constexpr int pre_tpr() {
   return D <= 32 ? 4 : D <= 64 ? 8 : 16;
 }
 
-// Row r < rows_q: D[r] = rowsum(dO * O) and, for bf16 inputs, fp16 copies of Q and dO; row
-// r < rows_k: fp16 copies of K and V (bf16 inputs). Rows are flattened over (b, h).
+// Row r < rows_q: D[r] = rowsum(dO * O) and, for bf16 inputs, fp16 copies of Q and dO. Rows are
+// flattened over (b, h). (K and V are converted by the dK/dV kernel, which holds them anyway.)
 template <int D, bool IS_BF16, bool O_F32>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, long long rows_q,
-                                                      long long rows_k) {
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, long long rows_q) {
   constexpr int TPR = pre_tpr<D>();
   constexpr int RPB = 256 / TPR;
   const int t = threadIdx.x;
@@ -94,12 +95,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, long long rows_
     if constexpr (IS_BF16) {
       st16(a.ws_q + base, to_f16x8<true>(ld16(static_cast<const uint16_t*>(a.q) + base)));
       st16(a.ws_do + base, to_f16x8<true>(dw));
-    }
-  }
-  if constexpr (IS_BF16) {
-    if (row < rows_k && cc < D / 8) {
-      st16(a.ws_k + base, to_f16x8<true>(ld16(static_cast<const uint16_t*>(a.k) + base)));
-      st16(a.ws_v + base, to_f16x8<true>(ld16(static_cast<const uint16_t*>(a.v) + base)));
     }
   }
 #pragma unroll
@@ -187,8 +182,9 @@ __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs 
   const size_t q_off = (size_t)bh * N * D;
   const size_t kv_off = (size_t)bh * Nk * D;
   const auto qrs = make_rsrc(a.q16 + q_off, (uint32_t)N * D * 2);
-  const auto krs = make_rsrc(a.k16 + kv_off, (uint32_t)Nk * D * 2);
-  const auto vrs = make_rsrc(a.v16 + kv_off, (uint32_t)Nk * D * 2);
+  // K and V in the input dtype: this kernel is the one that converts them (bf16 inputs).
+  const auto krs = make_rsrc(static_cast<const uint16_t*>(a.k) + kv_off, (uint32_t)Nk * D * 2);
+  const auto vrs = make_rsrc(static_cast<const uint16_t*>(a.v) + kv_off, (uint32_t)Nk * D * 2);
   const auto dors = make_rsrc(a.do16 + q_off, (uint32_t)N * D * 2);
   const auto lrs = make_rsrc(a.lse + (size_t)bh * N, (uint32_t)N * 4);
   const auto drs = make_rsrc(a.delta + (size_t)bh * N, (uint32_t)N * 4);
@@ -197,13 +193,30 @@ __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs 
   const int kw0 = k0 + wave * 32;  // this wave's first key
   const int key = kw0 + r;         // the key this lane owns in every accumulator
 
-  // K and V rows of this wave as B operands: key kw0 + r, d = 16*ks + 8*g .. +8.
+  // K and V rows of this wave as B operands: key kw0 + r, d = 16*ks + 8*g .. +8. bf16 inputs are
+  // converted to fp16 here (exact in range) and the fp16 rows written to the workspace, where
+  // the dQ kernel, launched after this one, streams them.
   Frag16 kf[C::KS], vf[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
     const uint32_t off = (uint32_t)(key * D + ks * 16 + g * 8) * 2;
     kf[ks].w = buf_ld16(krs, off);
     vf[ks].w = buf_ld16(vrs, off);
+  }
+  if constexpr (IS_BF16) {
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      kf[ks].w = to_f16x8<true>(kf[ks].w);
+      vf[ks].w = to_f16x8<true>(vf[ks].w);
+    }
+    if (key < Nk) {
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const size_t off = kv_off + (size_t)key * D + ks * 16 + g * 8;
+        st16(a.ws_k + off, kf[ks].w);
+        st16(a.ws_v + off, vf[ks].w);
+      }
+    }
   }
 
   f32x16 dvacc[C::DB], dkacc[C::DB];
@@ -673,16 +686,12 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
 template <int D, bool IS_BF16>
 static hipError_t launch_pre(const BwdArgs& a, bool o_f32, hipStream_t s) {
   const long long rows_q = (long long)a.bh * a.N;
-  const long long rows_k = (long long)a.bh * a.Nk;
-  const long long rows = rows_q > rows_k ? rows_q : rows_k;
   constexpr int RPB = 256 / pre_tpr<D>();
-  const int grid = (int)((rows + RPB - 1) / RPB);
+  const int grid = (int)((rows_q + RPB - 1) / RPB);
   if (o_f32)
-    hipLaunchKernelGGL((bwd_pre_kernel<D, IS_BF16, true>), dim3(grid), dim3(256), 0, s, a, rows_q,
-                       rows_k);
+    hipLaunchKernelGGL((bwd_pre_kernel<D, IS_BF16, true>), dim3(grid), dim3(256), 0, s, a, rows_q);
   else
-    hipLaunchKernelGGL((bwd_pre_kernel<D, IS_BF16, false>), dim3(grid), dim3(256), 0, s, a, rows_q,
-                       rows_k);
+    hipLaunchKernelGGL((bwd_pre_kernel<D, IS_BF16, false>), dim3(grid), dim3(256), 0, s, a, rows_q);
   return hipGetLastError();
 }
 

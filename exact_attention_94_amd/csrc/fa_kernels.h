@@ -45,8 +45,8 @@ struct BwdArgs {
   void* dv;
   float* delta;  // float32 [B,H,N]: rowsum(dO * O)
   // fp16 operands of the gradient kernels: the inputs themselves for fp16 inputs; for bf16
-  // inputs, the copies the preprocess kernel writes into the workspace (ws_q .. ws_do, which
-  // are null for fp16 inputs).
+  // inputs, fp16 copies in the workspace (ws_q .. ws_do, null for fp16 inputs): Q and dO written
+  // by the preprocess kernel, K and V by the dK/dV kernel (read by the dQ kernel after it).
   const uint16_t* q16;
   const uint16_t* k16;
   const uint16_t* v16;
