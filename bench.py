@@ -18,8 +18,12 @@ The line also carries the same step with dropout p = 0.1 ("dropout"), with a blo
 decoding of a long bf16 K/V cache ("decode": HBM bytes per second against the 8 TB/s peak); none
 of them is part of the headline value.
 
+The line also carries ("workloads") the forward and backward rates of the other named workloads:
+B=4 H=16 N=1024 d=64 (causal and not), B=1 H=32 N=8192 d=128 with peaked rows, and the
+B=1 H=8 N=32768 d=128 causal forward.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-dropout]
-                       [--no-blocksparse] [--no-decode]
+                       [--no-blocksparse] [--no-decode] [--no-workloads]
 """
 
 from __future__ import annotations
@@ -228,6 +232,82 @@ def time_blocksparse(fa, ev, stream, w, q, k, v, do, o, lse, grads, ws, steps):
             "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2)}
 
 
+def time_workloads(fa, ev, stream, dev, steps):
+    """The other named workloads, timed the same way (one event pair around `steps` back-to-back
+    calls): B=4 H=16 N=1024 d=64 forward, causal and not (O in bf16); B=1 H=32 N=8192 d=128 with
+    Q and K scaled by 2 (peaked rows), forward (fp32 O) and backward (fp32 gradients), causal;
+    B=1 H=8 N=32768 d=128 causal forward (O in bf16). Inputs are normal draws of the workloads'
+    shapes; FLOPs follow the headline convention."""
+    import torch
+    out = {}
+
+    def timed(fn, n):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = ev.create(), ev.create()
+        ev.record(e0, stream)
+        for _ in range(n):
+            fn()
+        ev.record(e1, stream)
+        torch.cuda.synchronize()
+        ms = ev.ms(e0, e1) / n
+        ev.destroy(e0)
+        ev.destroy(e1)
+        return ms
+
+    def rate(f, ms):
+        return {"ms": round(ms, 4), "tflops": round(f / (ms * 1e-3) / 1e12, 2),
+                "pct_peak": round(100 * f / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(1024)
+    B, H, N, d = 4, 16, 1024, 64
+    q, k, v = (torch.randn((B, H, N, d), device=dev, generator=g).to(torch.bfloat16)
+               for _ in range(3))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    f = 4.0 * B * H * N * N * d
+    row = {}
+    for causal in (True, False):
+        ms = timed(lambda: fa.forward(q, k, v, scale=d ** -0.5, causal=causal, out=o, lse=lse),
+                   steps)
+        row["fwd_causal" if causal else "fwd_noncausal"] = rate(f * (0.5 if causal else 1.0), ms)
+    out["B=4 H=16 N=1024 d=64 bf16"] = row
+    del q, k, v, o, lse
+
+    g.manual_seed(8192)
+    B, H, N, d = 1, 32, 8192, 128
+    q, k = ((2.0 * torch.randn((B, H, N, d), device=dev, generator=g)).to(torch.bfloat16)
+            for _ in range(2))
+    v, do = (torch.randn((B, H, N, d), device=dev, generator=g).to(torch.bfloat16)
+             for _ in range(2))
+    o = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    grads = tuple(torch.empty((B, H, N, d), dtype=torch.float32, device=dev) for _ in range(3))
+    ws = torch.empty(fa.workspace_bytes(B, H, N, d, fa.FA_BF16, fa.FA_F32), dtype=torch.uint8,
+                     device=dev)
+    f = 4.0 * B * H * N * N * d * 0.5
+    n = max(2, steps // 2)
+    ms_f = timed(lambda: fa.forward(q, k, v, scale=d ** -0.5, causal=True, out=o, lse=lse), n)
+    ms_b = timed(lambda: fa.backward(q, k, v, o, do, lse, scale=d ** -0.5, causal=True,
+                                     grad_dtype=torch.float32, workspace=ws, grads=grads), n)
+    out["B=1 H=32 N=8192 d=128 bf16 causal, Q and K x2"] = {"fwd": rate(f, ms_f),
+                                                             "bwd": rate(2.5 * f, ms_b)}
+    del q, k, v, do, o, lse, grads, ws
+
+    g.manual_seed(32768)
+    B, H, N, d = 1, 8, 32768, 128
+    q, k, v = (torch.randn((B, H, N, d), device=dev, generator=g).to(torch.bfloat16)
+               for _ in range(3))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    f = 4.0 * B * H * N * N * d * 0.5
+    ms = timed(lambda: fa.forward(q, k, v, scale=d ** -0.5, causal=True, out=o, lse=lse), n)
+    out["B=1 H=8 N=32768 d=128 bf16 causal"] = {"fwd": rate(f, ms)}
+    return out
+
+
 def time_decode(fa, ev, stream, dev, steps, B=4, H=32, nk=16384, d=128):
     """Split-KV decoding of one query row per sequence against a bf16 K/V cache of nk keys:
     HBM-bound, so the rate is bytes moved (K, V, Q read once, O and LSE written) per second
@@ -273,6 +353,8 @@ def main():
                     help="skip the extra timing of the block-sparse path")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the extra timing of split-KV decoding")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the timing of the other named workloads (N=1024, 8192, 32768)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -420,6 +502,8 @@ def main():
                                               steps=min(K, 10))
     if not args.no_decode:
         out["decode"] = time_decode(fa, ev, stream, dev, steps=min(K, 20))
+    if not args.no_workloads:
+        out["workloads"] = time_workloads(fa, ev, stream, dev, steps=min(K, 10))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, t, heads=args.cpu_heads)
     print(json.dumps(out), flush=True)

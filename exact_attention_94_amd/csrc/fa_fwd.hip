@@ -30,7 +30,8 @@
 //     query tiles of one (b, h) share an L2;
 //   * plain attention at d <= 128 runs fwd16pp_kernel: two groups of four waves that alternate
 //     a softmax phase and an MFMA phase, one phase apart, so that each SIMD always holds one wave
-//     of each kind. Dropout, block-sparse masks and d = 256 run fwd16_kernel (one group).
+//     of each kind, when its grid is large enough to fill the chip. Smaller grids, dropout,
+//     block-sparse masks and d = 256 run fwd16_kernel (one group).
 #include "fa_device.h"
 #include "fa_kernels.h"
 #include "fa_tune.h"
@@ -847,9 +848,18 @@ static hipError_t launch16pp(FwdArgs a, hipStream_t s) {
 template <int D, bool IS_BF16, bool O_F32, bool DROP, bool SPARSE>
 static hipError_t launch16_m(FwdArgs a, bool causal, hipStream_t s) {
   constexpr int QB = fwd_qb<D>();
-  if constexpr (!DROP && !SPARSE && D <= 128)
-    return causal ? launch16pp<D, IS_BF16, O_F32, true>(a, s)
-                  : launch16pp<D, IS_BF16, O_F32, false>(a, s);
+  if constexpr (!DROP && !SPARSE && D <= 128) {
+    // The two-group kernel's 256-query workgroups need enough of them to fill the chip: one per
+    // CU without a causal mask, two per CU with one (its workgroups differ in length). Below
+    // that (short sequences, few heads) the single-group kernel's 128-query workgroups give
+    // twice as many, and a causal grid's longest workgroup is half as long. Measured on MI355X:
+    // B=4 H=16 N=1024 d=64 causal 22 vs 25 us, non-causal 28 vs 26 us (two-group faster);
+    // B=1 H=16 N=1024 d=128 27 vs 36 us.
+    const long long pp_blocks = (long long)((a.N + FwdPP<D>::BR - 1) / FwdPP<D>::BR) * a.bh;
+    if (pp_blocks >= (causal ? kFwdPpMinBlocks : kFwdPpMinBlocks / 2))
+      return causal ? launch16pp<D, IS_BF16, O_F32, true>(a, s)
+                    : launch16pp<D, IS_BF16, O_F32, false>(a, s);
+  }
   return causal ? launch16<D, IS_BF16, O_F32, true, QB, DROP, SPARSE>(a, s)
                 : launch16<D, IS_BF16, O_F32, false, QB, DROP, SPARSE>(a, s);
 }

@@ -36,6 +36,12 @@
 #ifndef FA_DQ_PRE
 #define FA_DQ_PRE 4
 #endif
+// Fewest workgroups for which causal plain attention runs the two-group forward kernel (256
+// queries per workgroup; half as many suffice without a causal mask); smaller grids run the
+// single-group kernel (128 queries per workgroup).
+#ifndef FA_FWD_PP_MIN_BLOCKS
+#define FA_FWD_PP_MIN_BLOCKS 512
+#endif
 // Waves per SIMD the dQ kernel's register allocation must allow at d <= 64.
 #ifndef FA_DQ_WAVES_64
 #define FA_DQ_WAVES_64 2
@@ -58,6 +64,7 @@ constexpr int dq_pre() {
   return D == 64 ? FA_DQ_PRE : 0;
 }
 constexpr int kDqWaves64 = FA_DQ_WAVES_64;
+constexpr int kFwdPpMinBlocks = FA_FWD_PP_MIN_BLOCKS;
 
 template <int D>
 constexpr int fwd_tile_keys() {
