@@ -134,6 +134,18 @@ def test_forward_sweep(fa, dtype, d, causal):
             _fwd_case(fa, (B, H, n, d), dtype, causal, seed=n * 7 + d)
 
 
+# Grids large enough for the two-group forward kernel (causal: >= 512 workgroups of 256 queries,
+# non-causal: >= 256), with a ragged last query tile (1000 = 3 * 256 + 232) and a ragged last key
+# tile; the small sweeps above run the single-group kernel.
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_two_group_ragged(fa, dtype, d, causal):
+    B, H = (4, 32) if causal else (2, 32)
+    print(f"  B={B} H={H} N=1000 d={d}", flush=True)
+    _fwd_case(fa, (B, H, 1000, d), dtype, causal, seed=1000 + d)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_forward_sweep_d256(fa, dtype, causal):
