@@ -18,12 +18,19 @@ The line also carries the same step with dropout p = 0.1 ("dropout"), with a blo
 decoding of a long bf16 K/V cache ("decode": HBM bytes per second against the 8 TB/s peak); none
 of them is part of the headline value.
 
+Before timing, W warm-up steps run and then untimed steps continue for --settle-ms (default
+500 ms): the first tens of milliseconds of load from idle run ~15% slower than the steady state.
+
+Next to the mean step time the line gives the median and minimum of the per-step times of the
+breakdown loop, the mean step time with the caches flushed before each step (cold_step_ms), and
+the shader clock rocm-smi reports after the timing (gpu_sclk_mhz).
+
 The line also carries ("workloads") the forward and backward rates of the other named workloads:
 B=4 H=16 N=1024 d=64 (causal and not), B=1 H=32 N=8192 d=128 with peaked rows, and the
 B=1 H=8 N=32768 d=128 causal forward.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-dropout]
-                       [--no-blocksparse] [--no-decode] [--no-workloads]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS] [--no-cpu-baseline]
+                       [--no-dropout] [--no-blocksparse] [--no-decode] [--no-workloads]
 """
 
 from __future__ import annotations
@@ -232,6 +239,47 @@ def time_blocksparse(fa, ev, stream, w, q, k, v, do, o, lse, grads, ws, steps):
             "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2)}
 
 
+def time_cold(ev, stream, dev, step, steps):
+    """Mean step time with the caches flushed before every step: a 512 MiB buffer is written
+    between steps (outside the timed events), so the inputs start in HBM rather than in the
+    256 MB last-level cache."""
+    import torch
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    total = 0.0
+    for _ in range(steps):
+        flush.fill_(1)
+        e0, e1 = ev.create(), ev.create()
+        ev.record(e0, stream)
+        step()
+        ev.record(e1, stream)
+        torch.cuda.synchronize()
+        total += ev.ms(e0, e1)
+        ev.destroy(e0)
+        ev.destroy(e1)
+    return total / steps
+
+
+def gpu_clock_mhz():
+    """Current shader clock of GPU 0 as reported by rocm-smi (None if it is not available)."""
+    import shutil
+    import subprocess
+    exe = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
+    try:
+        res = subprocess.run([exe, "--showclocks", "--json"], capture_output=True, text=True,
+                             timeout=20)
+        data = json.loads(res.stdout)
+    except Exception:
+        return None
+    for card in data.values():
+        if isinstance(card, dict):
+            for key, val in card.items():
+                if "sclk" in key.lower():
+                    m = re.search(r"(\d+)\s*Mhz", str(val), re.I)
+                    if m:
+                        return int(m.group(1))
+    return None
+
+
 def time_workloads(fa, ev, stream, dev, steps):
     """The other named workloads, timed the same way (one event pair around `steps` back-to-back
     calls): B=4 H=16 N=1024 d=64 forward, causal and not (O in bf16); B=1 H=32 N=8192 d=128 with
@@ -345,6 +393,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=500.0,
+                    help="after the warm-up steps, keep running untimed steps for this long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--no-dropout", action="store_true",
@@ -408,6 +458,16 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # Settle: the first tens of milliseconds of sustained load run ~15% slower (clocks and power
+    # state still ramping from idle), so untimed steps continue until the GPU has been busy for
+    # at least --settle-ms.
+    t_settle = time.perf_counter()
+    settle_steps = 0
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms and settle_steps < 5000:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        settle_steps += 10
 
     ev = HipEvents()
     K = args.steps
@@ -447,6 +507,9 @@ def main():
     fwd_ms = sum(ev.ms(ef0[i], ef1[i]) for i in range(K)) / K
     bwd_ms = sum(ev.ms(ef1[i], eb2[i]) for i in range(K)) / K
     main_ms = sum(ev.ms(eb0[i], eb1[i]) for i in range(K)) / K
+    per_step = sorted(ev.ms(ef0[i], eb2[i]) for i in range(K))
+    step_median_ms = per_step[K // 2] if K % 2 else 0.5 * (per_step[K // 2 - 1] + per_step[K // 2])
+    step_min_ms = per_step[0]
     for e in [e_start, e_end] + ef0 + ef1 + eb0 + eb1 + eb2:
         ev.destroy(e)
     assert torch.isfinite(o).all() and all(torch.isfinite(g).all() for g in grads)
@@ -457,6 +520,7 @@ def main():
     f_dkdv = 2.0 * f_fwd  # S, dP, dV, dK
     main_tf = tf(f_dkdv, main_ms)
     traffic = measured_traffic()
+    cold = time_cold(ev, stream, dev, step, steps=min(K, 10))
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -464,6 +528,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": round(step_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -482,6 +547,10 @@ def main():
         "bwd_ms": round(bwd_ms, 4),
         "step_pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "host_wall_ms_per_step": round(1e3 * t_wall / K, 4),
+        "step_ms_median": round(step_median_ms, 4),
+        "step_ms_min": round(step_min_ms, 4),
+        "cold_step_ms": round(cold, 4),
+        "gpu_sclk_mhz": gpu_clock_mhz(),
         "roofline": {
             "kernel": "bwd_dkdv_kernel<64, bf16, f32 grads, causal>",
             "bound": "mfma",
