@@ -51,6 +51,29 @@ def test_forward_kv_sweep(fa, dtype, d, causal):
             check("LSE", host64(lse), l_ref, 1e-3)
 
 
+# A grid large enough for the two-group forward kernel (4 query tiles of 256 x 128 heads = 512
+# workgroups), so that its query offset (causal: Nk - Nq) and key count Nk != Nq are exercised;
+# ragged last query and key tiles (1000 = 3 * 256 + 232, 1500 = 11 * 128 + 92).
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_kv_two_group_grid(fa, dtype, d, causal):
+    import torch
+    B, H, nq, nk = 4, 32, 1000, 1500
+    tq = inp.draw((B, H, nq, d), dtype, 9000 + d)
+    tk = inp.draw((B, H, nk, d), dtype, 9001 + d)
+    q = to_device(tq["q"])
+    k, v = to_device(tk["k"]), to_device(tk["v"])
+    out = nan_like((B, H, nq, d), torch.float32)
+    lse = nan_like((B, H, nq), torch.float32)
+    scale = 1.0 / math.sqrt(d)
+    fa.forward(q, k, v, scale=scale, causal=causal, out=out, lse=lse)
+    torch.cuda.synchronize()
+    o_ref, l_ref = attn_decode_ref(tq["q"].values, tk["k"].values, tk["v"].values, scale, causal)
+    check("O", host64(out), o_ref, 2e-2)
+    check("LSE", host64(lse), l_ref, 1e-3)
+
+
 def test_forward_kv_is_the_tail_of_the_full_causal_forward(fa):
     """Rows N-Nq.. of a causal forward over N positions, recomputed from only those query rows
     against all N keys, are bitwise the same: each row visits the same key tiles in the same
