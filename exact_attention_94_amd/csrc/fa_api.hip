@@ -3,6 +3,7 @@
 // nothing and touches no device state.
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "../../include/fa.h"
 #include "fa_kernels.h"
@@ -55,20 +56,53 @@ bool make_drop(float p, uint64_t seed, uint32_t offset, fa::DropParams& dp) {
   return true;
 }
 
-// Workspace: D (fp32 [B,H,Nq]) | for bf16 inputs, fp16 copies of Q ([B,H,Nq,d]), K and V
-// ([B,H,Nk,d] each) and dO ([B,H,Nq,d]); the copies start 256 bytes aligned.
+// Workspace, each section 256-byte aligned: D (fp32 [B,H,Nq]) | the per-head dO scale 2^-s
+// (fp32 [B,H]) | partial maxima of |dO| (kMaxParts words per head) | a debug flag word |
+// fp16 copies: dO ([B,H,Nq,d]) always; for bf16 inputs also Q ([B,H,Nq,d]), K and V
+// ([B,H,Nk,d] each).
 struct WsLayout {
-  size_t f16_off, q_elems, k_elems, total;
+  size_t gscale_off, dmax_off, flag_off, f16_off, q_elems, k_elems, total;
 };
 
 WsLayout workspace_layout(int B, int H, int Nq, int Nk, int d, fa_dtype in_dtype) {
-  const size_t rows = (size_t)B * H * Nq;
+  const size_t bh = (size_t)B * H;
+  const size_t rows = bh * Nq;
   WsLayout w;
   w.q_elems = rows * (size_t)d;
-  w.k_elems = (size_t)B * H * Nk * (size_t)d;
-  w.f16_off = round_up(rows * sizeof(float), 256);
-  w.total = w.f16_off + ((in_dtype == FA_BF16) ? (2 * w.q_elems + 2 * w.k_elems) * 2 : 0);
+  w.k_elems = bh * Nk * (size_t)d;
+  w.gscale_off = round_up(rows * sizeof(float), 256);
+  w.dmax_off = w.gscale_off + round_up(bh * sizeof(float), 256);
+  w.flag_off = w.dmax_off + round_up(bh * fa::kMaxParts * sizeof(uint32_t), 256);
+  w.f16_off = w.flag_off + 256;
+  const size_t f16_elems =
+      w.q_elems + ((in_dtype == FA_BF16) ? (w.q_elems + 2 * w.k_elems) : 0);
+  w.total = w.f16_off + f16_elems * 2;
   return w;
+}
+
+// Argument checks shared by the backward entry points and their workspace-size queries
+// (shapes, dtypes and the mode restrictions). FA_OK if fa_backward* would accept them.
+fa_status backward_dtypes_ok(int B, int H, int N, int Nk, int d, fa_dtype in_dtype,
+                             fa_dtype o_dtype, fa_dtype grad_dtype, bool extra_mode) {
+  if (!valid_dtype(in_dtype) || !valid_dtype(o_dtype) || !valid_dtype(grad_dtype))
+    return FA_ERR_INVALID_ARG;
+  const fa_status st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (Nk != 0) {
+    const fa_status sk = check_shape(B, H, Nk, d);
+    if (sk != FA_OK) return sk;
+  }
+  if (in_dtype == FA_F32 || d == 256) return FA_ERR_UNSUPPORTED;
+  if (o_dtype != in_dtype && o_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if (grad_dtype != in_dtype && grad_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if (Nk != 0 && extra_mode) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+// FA_DEBUG_CHECKS=1 in the environment turns on the input range check of the backward.
+bool debug_checks() {
+  const char* e = getenv("FA_DEBUG_CHECKS");
+  return e != nullptr && e[0] == '1' && e[1] == '\0';
 }
 
 }  // namespace
@@ -82,6 +116,7 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim, dtype combination or mode not provided by this library";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case FA_ERR_HIP: return "FA_ERR_HIP: a HIP runtime call or kernel launch failed";
+    case FA_ERR_RANGE: return "FA_ERR_RANGE: an input value lies outside the range the backward's fp16 operands hold (|x| >= 65536 or not finite; found by the FA_DEBUG_CHECKS=1 range check)";
   }
   return "unknown fa_status";
 }
@@ -163,25 +198,36 @@ fa_status backward_impl(const void* q, const void* k, const void* v, const void*
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
       !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return FA_ERR_INVALID_ARG;
-  if (!valid_dtype(in_dtype) || !valid_dtype(o_dtype) || !valid_dtype(grad_dtype))
-    return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
-  const fa_status st = check_shape(B, H, N, d);
+  const fa_status st = backward_dtypes_ok(B, H, N, Nk, d, in_dtype, o_dtype, grad_dtype,
+                                          drop != nullptr || sparse != nullptr);
   if (st != FA_OK) return st;
-  if (in_dtype == FA_F32 || d == 256) return FA_ERR_UNSUPPORTED;
-  if (o_dtype != in_dtype && o_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
-  if (grad_dtype != in_dtype && grad_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
-  if (Nk != 0) {
-    const fa_status sk = check_shape(B, H, Nk, d);
-    if (sk != FA_OK) return sk;
-    if (causal && N > Nk) return FA_ERR_INVALID_ARG;
-    if (drop || sparse) return FA_ERR_UNSUPPORTED;
-  }
+  if (Nk != 0 && causal && N > Nk) return FA_ERR_INVALID_ARG;
   const int nk = Nk != 0 ? Nk : N;
   const WsLayout ws = workspace_layout(B, H, N, nk, d, in_dtype);
   if (!workspace || !aligned16(workspace) || workspace_bytes < ws.total) return FA_ERR_WORKSPACE;
   char* wsb = static_cast<char*>(workspace);
+
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+
+  // Debug range check (FA_DEBUG_CHECKS=1): bf16 Q, K and V become fp16 operands, which hold
+  // |x| < 65520 only; a value beyond that would turn into an infinity and silently spoil the
+  // gradients. The check runs before any backward kernel and waits for its answer. (dO needs no
+  // check: it is scaled per head into fp16's range.)
+  if (in_dtype == FA_BF16 && debug_checks()) {
+    uint32_t* flag = reinterpret_cast<uint32_t*>(wsb + ws.flag_off);
+    uint32_t host_flag = 0;
+    if (fa::launch_clear_flag(flag, hs) != hipSuccess ||
+        fa::launch_range_check_bf16(q, ws.q_elems, flag, hs) != hipSuccess ||
+        fa::launch_range_check_bf16(k, ws.k_elems, flag, hs) != hipSuccess ||
+        fa::launch_range_check_bf16(v, ws.k_elems, flag, hs) != hipSuccess ||
+        hipMemcpyAsync(&host_flag, flag, sizeof(host_flag), hipMemcpyDeviceToHost, hs) !=
+            hipSuccess ||
+        hipStreamSynchronize(hs) != hipSuccess)
+      return FA_ERR_HIP;
+    if (host_flag != 0) return FA_ERR_RANGE;
+  }
 
   fa::BwdArgs a{};
   a.q = q;
@@ -191,21 +237,22 @@ fa_status backward_impl(const void* q, const void* k, const void* v, const void*
   a.dout = dout;
   a.lse = lse;
   a.delta = static_cast<float*>(workspace);
+  a.gscale = reinterpret_cast<float*>(wsb + ws.gscale_off);
+  a.dmax = reinterpret_cast<uint32_t*>(wsb + ws.dmax_off);
+  uint16_t* f16 = reinterpret_cast<uint16_t*>(wsb + ws.f16_off);
+  a.ws_do = f16;
+  a.do16 = a.ws_do;
   if (in_dtype == FA_BF16) {
-    uint16_t* f16 = reinterpret_cast<uint16_t*>(wsb + ws.f16_off);
-    a.ws_q = f16;
+    a.ws_q = a.ws_do + ws.q_elems;
     a.ws_k = a.ws_q + ws.q_elems;
     a.ws_v = a.ws_k + ws.k_elems;
-    a.ws_do = a.ws_v + ws.k_elems;
     a.q16 = a.ws_q;
     a.k16 = a.ws_k;
     a.v16 = a.ws_v;
-    a.do16 = a.ws_do;
   } else {
     a.q16 = static_cast<const uint16_t*>(q);
     a.k16 = static_cast<const uint16_t*>(k);
     a.v16 = static_cast<const uint16_t*>(v);
-    a.do16 = static_cast<const uint16_t*>(dout);
   }
   a.dq = dq;
   a.dk = dk;
@@ -226,8 +273,7 @@ fa_status backward_impl(const void* q, const void* k, const void* v, const void*
     mode = fa::Mode::kSparse;
   }
   const hipError_t e = fa::launch_backward(a, d, (int)in_dtype, (int)o_dtype, (int)grad_dtype,
-                                           causal != 0, mode, static_cast<hipStream_t>(stream),
-                                           t_prof_before, t_prof_after);
+                                           causal != 0, mode, hs, t_prof_before, t_prof_after);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -275,16 +321,14 @@ fa_status fa_forward_blocksparse(const void* q, const void* k, const void* v, vo
 
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d, fa_dtype in_dtype,
                                    fa_dtype grad_dtype) {
-  if (check_shape(B, H, N, d) != FA_OK || d == 256 || !valid_dtype(in_dtype) ||
-      !valid_dtype(grad_dtype))
-    return 0;
+  // o_dtype = in_dtype is always accepted, so it does not narrow the check.
+  if (backward_dtypes_ok(B, H, N, 0, d, in_dtype, in_dtype, grad_dtype, false) != FA_OK) return 0;
   return workspace_layout(B, H, N, N, d, in_dtype).total;
 }
 
 size_t fa_backward_kv_workspace_bytes(int B, int H, int Nq, int Nk, int d, fa_dtype in_dtype,
                                       fa_dtype grad_dtype) {
-  if (check_shape(B, H, Nq, d) != FA_OK || check_shape(B, H, Nk, d) != FA_OK || d == 256 ||
-      !valid_dtype(in_dtype) || !valid_dtype(grad_dtype))
+  if (Nk < 1 || backward_dtypes_ok(B, H, Nq, Nk, d, in_dtype, in_dtype, grad_dtype, false) != FA_OK)
     return 0;
   return workspace_layout(B, H, Nq, Nk, d, in_dtype).total;
 }

@@ -8,8 +8,11 @@
 // No N x N matrix is ever written to memory.
 //
 // Kernels (one stream, in order):
-//   1. bwd_pre:   D = rowsum(dO * O) in fp32 from the forward's output; for bf16 inputs, fp16
-//                 copies of Q and dO in the workspace.
+//   1. bwd_absmax: per-head max |dO| (partial maxima, no atomics); for bf16 inputs, the fp16 copy
+//                 of Q in the workspace.
+//      bwd_pre:   the head's dO scale 2^s (a power of two, 1 for ordinary gradients) from those
+//                 maxima; D = 2^s rowsum(dO * O) in fp32 from the forward's output and the fp16
+//                 copy of 2^s dO. The gradient epilogues multiply by 2^-s, which is exact.
 //   2. bwd_dkdv:  keys outer. One workgroup per tile of 128 keys (4 waves x 32 keys) keeps dK and
 //                 dV in registers over all query tiles (causal: those at or below the
 //                 diagonal): S, dP, then P, dS, then dV += P^T dO and dK += dS^T Q. For bf16
@@ -23,10 +26,12 @@
 // on this chip those fp32 atomics each reach the memory side (measured: they were 42% of the
 // fused kernel's time at B=2 H=16 N=4096 d=64 causal). The result is also deterministic.
 //
-// All products run on v_mfma_f32_32x32x16_f16 with fp32 accumulation. bf16 inputs are converted
-// once to fp16 by bwd_pre (exact while 2^-14 <= |x| <= 65504); P and dS are rounded to fp16,
-// whose 11-bit significand keeps the gradients of long peaked rows inside the error budget that
-// bf16 operands would exceed. Operands that a product needs transposed are read from row-major
+// All products run on v_mfma_f32_32x32x16_f16 with fp32 accumulation. bf16 Q, K and V are
+// converted once to fp16 (exact while 2^-14 <= |x| <= 65504; larger values are outside the
+// supported range); dO is scaled per head so that its largest magnitude, and with it dP and dS,
+// sits well inside fp16's range whatever the size of the upstream gradient. P and dS are rounded
+// to fp16, whose 11-bit significand keeps the gradients of long peaked rows inside the error
+// budget that bf16 operands would exceed. Operands that a product needs transposed are read from row-major
 // LDS tiles with ds_read_b64_tr_b16, so every tile is staged once, in one layout. Streamed tiles
 // (Q / dO in the dK/dV kernel, K / V in the dQ kernel) reach LDS by direct buffer->LDS loads,
 // issued one step ahead, into unpadded rows with the chunk swizzle of swz_off.
@@ -59,18 +64,74 @@ constexpr int pre_tpr() {
   return D <= 32 ? 4 : D <= 64 ? 8 : 16;
 }
 
-// Row r < rows_q: D[r] = rowsum(dO * O) and, for bf16 inputs, fp16 copies of Q and dO. Rows are
-// flattened over (b, h). (K and V are converted by the dK/dV kernel, which holds them anyway.)
+// Largest value of x over the workgroup (256 threads), returned to every thread.
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t x, uint32_t* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  return max(max(red[0], red[1]), max(red[2], red[3]));
+}
+
+// 1a. Max pass. Workgroup bh * n_parts + p covers elements [p * chunk, (p + 1) * chunk) of head
+// bh (chunk a multiple of 2048) and writes the largest |dO| there, as the 16-bit magnitude
+// pattern (for bf16 and fp16 alike, larger magnitudes have larger patterns), to dmax[bh][p].
+// For bf16 inputs it also writes the fp16 copy of the same elements of Q.
+template <int D, bool IS_BF16>
+__global__ __launch_bounds__(256) void bwd_absmax_kernel(BwdArgs a, int chunk, int n_parts) {
+  __shared__ uint32_t red[4];
+  const int bh = blockIdx.x / n_parts;
+  const int p = blockIdx.x - bh * n_parts;
+  const size_t head = (size_t)bh * a.N * D;
+  const int n = a.N * D;
+  const int beg = p * chunk;
+  const int end = min(n, beg + chunk);
+  const uint16_t* dout = static_cast<const uint16_t*>(a.dout) + head;
+  uint32_t mx = 0;
+  for (int e = beg + (int)threadIdx.x * 8; e < end; e += 2048) {
+    const u32x4 w = ld16(dout + e);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx = max(mx, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+    if constexpr (IS_BF16)
+      st16(a.ws_q + head + e, to_f16x8<true>(ld16(static_cast<const uint16_t*>(a.q) + head + e)));
+  }
+  mx = block_max_u32(mx, red);
+  if (threadIdx.x == 0) a.dmax[(size_t)bh * kMaxParts + p] = mx;
+}
+
+// Exponent s of the dO scale of a head whose largest |dO| is amax: 0 while amax lies in
+// [1/2, 16] (ordinary gradients keep their bits), otherwise the s that brings amax into [8, 16),
+// clamped to [-120, 120] so that 2^s and 2^-s are normal floats. amax = 0 gives s = 0.
+__device__ __forceinline__ int do_scale_exp(float amax) {
+  if (!(amax > 0.f) || (amax >= 0.5f && amax <= 16.f)) return 0;
+  int ex;
+  frexpf(amax, &ex);  // amax = f * 2^ex, f in [1/2, 1)
+  return min(120, max(-120, 4 - ex));
+}
+
+// 1b. Preprocess, workgroup bh * n_rb + rb (row block rb of head bh): the head's dO scale 2^s
+// from the partial maxima, then for each row of the block D = 2^s rowsum(dO * O) in fp32 and the
+// fp16 copy of dO * 2^s (exact scaling, one rounding). Row block 0 stores 2^-s for the gradient
+// epilogues.
 template <int D, bool IS_BF16, bool O_F32>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, long long rows_q) {
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, int n_parts, int n_rb) {
   constexpr int TPR = pre_tpr<D>();
   constexpr int RPB = 256 / TPR;
+  __shared__ uint32_t red[4];
   const int t = threadIdx.x;
-  const long long row = (long long)blockIdx.x * RPB + t / TPR;
+  const int bh = blockIdx.x / n_rb;
+  const int rb = blockIdx.x - bh * n_rb;
+  const uint32_t part = t < n_parts ? a.dmax[(size_t)bh * kMaxParts + t] : 0u;
+  const float amax = to_f32<IS_BF16>((uint16_t)block_max_u32(part, red));
+  const int sexp = do_scale_exp(amax);
+  const float up = ldexpf(1.f, sexp);
+  if (rb == 0 && t == 0) a.gscale[bh] = ldexpf(1.f, -sexp);
+
+  const int row = rb * RPB + t / TPR;
   const int cc = t % TPR;
-  const size_t base = (size_t)row * D + cc * 8;
+  const size_t base = ((size_t)bh * a.N + row) * D + cc * 8;
   float acc = 0.f;
-  if (row < rows_q && cc < D / 8) {
+  if (row < a.N && cc < D / 8) {
     const u32x4 dw = ld16(static_cast<const uint16_t*>(a.dout) + base);
     float dof[8];
 #pragma unroll
@@ -92,14 +153,44 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, long long rows_
         acc += dof[2 * w + 1] * to_f32<IS_BF16>((uint16_t)(ow[w] >> 16));
       }
     }
-    if constexpr (IS_BF16) {
-      st16(a.ws_q + base, to_f16x8<true>(ld16(static_cast<const uint16_t*>(a.q) + base)));
-      st16(a.ws_do + base, to_f16x8<true>(dw));
-    }
+    u32x4 o16;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) o16[w] = pack2<false>(dof[2 * w] * up, dof[2 * w + 1] * up);
+    st16(a.ws_do + base, o16);
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows_q && cc == 0) a.delta[row] = acc;
+  if (row < a.N && cc == 0) a.delta[(size_t)bh * a.N + row] = acc * up;
+}
+
+// Debug range check (see fa_kernels.h).
+__global__ __launch_bounds__(256) void clear_flag_kernel(uint32_t* flag) { *flag = 0u; }
+
+__global__ __launch_bounds__(256) void range_check_bf16_kernel(const uint16_t* x, size_t n,
+                                                               uint32_t* flag) {
+  bool bad = false;
+  for (size_t e = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8; e < n;
+       e += (size_t)gridDim.x * 256 * 8) {
+    // n is a multiple of 8 (d >= 32), so whole 16-byte vectors stay in bounds.
+    const u32x4 w = ld16(x + e);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      bad |= ((w[i] & 0x7FFFu) >= 0x4780u) || (((w[i] >> 16) & 0x7FFFu) >= 0x4780u);
+  }
+  if (bad) *flag = 1u;
+}
+
+hipError_t launch_clear_flag(uint32_t* flag, hipStream_t s) {
+  hipLaunchKernelGGL(clear_flag_kernel, dim3(1), dim3(1), 0, s, flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_range_check_bf16(const void* x, size_t n, uint32_t* flag, hipStream_t s) {
+  const size_t vecs = (n + 7) / 8;
+  const int grid = (int)min((size_t)2048, (vecs + 255) / 256);
+  hipLaunchKernelGGL(range_check_bf16_kernel, dim3(grid), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(x), n, flag);
+  return hipGetLastError();
 }
 
 // Row placement inside a 32-row block of a staged tile: LDS row r holds element
@@ -435,20 +526,22 @@ __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs 
     __syncthreads();
   }
 
-  // Epilogue: dK = scale * (dK^T acc), dV = dV^T acc; accumulator rows are d, the column is
-  // this lane's key.
+  // Epilogue: dK = scale * 2^-s (dK^T acc), dV = 2^-s (dV^T acc), 2^-s undoing the head's dO
+  // scale; accumulator rows are d, the column is this lane's key.
+  const float gs = a.gscale[bh];
+  const float ks_ = a.scale * gs;
   if (key < Nk) {
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
         const size_t off = kv_off + (size_t)key * D + db * 32 + blk * 8 + g * 4;
-        store_grad4<G_F32, IS_BF16>(a.dk, off, dkacc[db][blk * 4] * a.scale,
-                                    dkacc[db][blk * 4 + 1] * a.scale,
-                                    dkacc[db][blk * 4 + 2] * a.scale,
-                                    dkacc[db][blk * 4 + 3] * a.scale);
-        store_grad4<G_F32, IS_BF16>(a.dv, off, dvacc[db][blk * 4], dvacc[db][blk * 4 + 1],
-                                    dvacc[db][blk * 4 + 2], dvacc[db][blk * 4 + 3]);
+        store_grad4<G_F32, IS_BF16>(a.dk, off, dkacc[db][blk * 4] * ks_,
+                                    dkacc[db][blk * 4 + 1] * ks_, dkacc[db][blk * 4 + 2] * ks_,
+                                    dkacc[db][blk * 4 + 3] * ks_);
+        store_grad4<G_F32, IS_BF16>(a.dv, off, dvacc[db][blk * 4] * gs,
+                                    dvacc[db][blk * 4 + 1] * gs, dvacc[db][blk * 4 + 2] * gs,
+                                    dvacc[db][blk * 4 + 3] * gs);
       }
     }
   }
@@ -664,18 +757,18 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
     __syncthreads();
   }
 
-  // Epilogue: dQ = scale * dQ^T acc; accumulator rows are d = 32db + 8(i/4) + 4g + i%4, the
-  // column is this lane's query.
+  // Epilogue: dQ = scale * 2^-s (dQ^T acc), 2^-s undoing the head's dO scale; accumulator rows
+  // are d = 32db + 8(i/4) + 4g + i%4, the column is this lane's query.
+  const float qs_ = a.scale * a.gscale[bh];
   if (qrow < N) {
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
         const size_t off = q_off + (size_t)qrow * D + db * 32 + blk * 8 + g * 4;
-        store_grad4<G_F32, IS_BF16>(a.dq, off, dqacc[db][blk * 4] * a.scale,
-                                    dqacc[db][blk * 4 + 1] * a.scale,
-                                    dqacc[db][blk * 4 + 2] * a.scale,
-                                    dqacc[db][blk * 4 + 3] * a.scale);
+        store_grad4<G_F32, IS_BF16>(a.dq, off, dqacc[db][blk * 4] * qs_,
+                                    dqacc[db][blk * 4 + 1] * qs_, dqacc[db][blk * 4 + 2] * qs_,
+                                    dqacc[db][blk * 4 + 3] * qs_);
       }
   }
 }
@@ -683,15 +776,31 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
 // ----------------------------------------------------------------------------------------
 // Launchers.
 // ----------------------------------------------------------------------------------------
+// Elements per workgroup of the max pass: the head split into at most kMaxParts slices of a
+// multiple of 2048 elements (256 threads x 8).
+inline int absmax_chunk(long long head_elems) {
+  const long long per = (head_elems + kMaxParts - 1) / kMaxParts;
+  return (int)((per + 2047) / 2048 * 2048);
+}
+
 template <int D, bool IS_BF16>
 static hipError_t launch_pre(const BwdArgs& a, bool o_f32, hipStream_t s) {
-  const long long rows_q = (long long)a.bh * a.N;
+  const long long head_elems = (long long)a.N * D;
+  const int chunk = absmax_chunk(head_elems);
+  const int n_parts = (int)((head_elems + chunk - 1) / chunk);
+  hipLaunchKernelGGL((bwd_absmax_kernel<D, IS_BF16>), dim3(n_parts * a.bh), dim3(256), 0, s, a,
+                     chunk, n_parts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   constexpr int RPB = 256 / pre_tpr<D>();
-  const int grid = (int)((rows_q + RPB - 1) / RPB);
+  const int n_rb = (a.N + RPB - 1) / RPB;
+  const dim3 grid(n_rb * a.bh);
   if (o_f32)
-    hipLaunchKernelGGL((bwd_pre_kernel<D, IS_BF16, true>), dim3(grid), dim3(256), 0, s, a, rows_q);
+    hipLaunchKernelGGL((bwd_pre_kernel<D, IS_BF16, true>), grid, dim3(256), 0, s, a, n_parts,
+                       n_rb);
   else
-    hipLaunchKernelGGL((bwd_pre_kernel<D, IS_BF16, false>), dim3(grid), dim3(256), 0, s, a, rows_q);
+    hipLaunchKernelGGL((bwd_pre_kernel<D, IS_BF16, false>), grid, dim3(256), 0, s, a, n_parts,
+                       n_rb);
   return hipGetLastError();
 }
 

@@ -43,10 +43,17 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;  // float32 [B,H,N]: rowsum(dO * O)
-  // fp16 operands of the gradient kernels: the inputs themselves for fp16 inputs; for bf16
-  // inputs, fp16 copies in the workspace (ws_q .. ws_do, null for fp16 inputs): Q and dO written
-  // by the preprocess kernel, K and V by the dK/dV kernel (read by the dQ kernel after it).
+  float* delta;  // float32 [B,H,N]: rowsum(dO * O) * 2^s_bh (the head's dO scale, below)
+  // Per-head power-of-two scaling of dO: the fp16 operand copy of dO holds dO * 2^s_bh, chosen
+  // from the head's max |dO| so that small or large upstream gradients keep fp16's precision;
+  // gscale[bh] = 2^-s_bh undoes it in the gradient epilogues. dmax holds kMaxParts partial
+  // maxima of |dO| per head (16-bit magnitude patterns) for the preprocess to reduce.
+  float* gscale;
+  uint32_t* dmax;
+  // fp16 operands of the gradient kernels: Q, K and V are the inputs themselves for fp16 inputs
+  // and fp16 copies in the workspace for bf16 inputs (ws_q written by the max pass, ws_k and
+  // ws_v by the dK/dV kernel for the dQ kernel after it; null for fp16 inputs); dO is always the
+  // scaled fp16 copy ws_do written by the preprocess.
   const uint16_t* q16;
   const uint16_t* k16;
   const uint16_t* v16;
@@ -65,6 +72,9 @@ struct BwdArgs {
   DropParams drop;  // used only by the dropout instances
   SparseParams sparse;  // used only by the block-sparse instances
 };
+
+// Partial maxima of |dO| per head (one per workgroup of the max pass).
+constexpr int kMaxParts = 256;
 
 // Split-KV decoding: Nq (<= 4) query rows per head against Nk keys; partials per (head, chunk).
 struct DecArgs {
@@ -97,5 +107,11 @@ hipError_t launch_forward(const FwdArgs& a, int d, int in_dtype, int o_f32, bool
 hipError_t launch_backward(const BwdArgs& a, int d, int in_dtype, int o_dtype, int grad_dtype,
                            bool causal, Mode mode, hipStream_t s, hipEvent_t ev_before,
                            hipEvent_t ev_after);
+
+// Debug range check of 16-bit inputs bound for fp16 operands: sets *flag to 1 if any of the n
+// 16-bit bf16 values at x has a magnitude fp16 cannot hold (|x| >= 65536 after rounding, or not
+// finite). *flag must be zero beforehand (clear_flag).
+hipError_t launch_clear_flag(uint32_t* flag, hipStream_t s);
+hipError_t launch_range_check_bf16(const void* x, size_t n, uint32_t* flag, hipStream_t s);
 
 }  // namespace fa

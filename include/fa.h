@@ -32,7 +32,8 @@
  * Errors: arguments are validated before any launch. An unsupported combination returns
  * FA_ERR_UNSUPPORTED and an invalid one FA_ERR_INVALID_ARG; nothing is launched and there is no
  * fallback path. FA_ERR_HIP reports a failed HIP call or launch. The library never aborts,
- * prints or throws across this boundary.
+ * prints or throws across this boundary. FA_ERR_RANGE is returned only by the optional debug
+ * range check of the backward (FA_DEBUG_CHECKS=1, see the input range note below).
  *
  * Asynchrony: calls enqueue kernels on `stream` (a hipStream_t; NULL = the null stream) and
  * return without waiting. Calls on distinct streams may run concurrently from distinct threads.
@@ -52,7 +53,9 @@ typedef enum fa_status {
   FA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, size overflow, non-finite scale */
   FA_ERR_UNSUPPORTED = 2, /* head dim, dtype combination or mode this build does not provide */
   FA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than fa_backward_workspace_bytes() */
-  FA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+  FA_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+  FA_ERR_RANGE = 5        /* FA_DEBUG_CHECKS=1 only: a bf16 input of a backward call lies outside
+                             the range of its fp16 operand copy (|x| >= 65536 or not finite) */
 } fa_status;
 
 typedef enum fa_dtype { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
@@ -87,12 +90,30 @@ fa_status fa_forward_kv(const void* q, const void* k, const void* v, void* o, fl
 
 /*
  * Bytes of device workspace fa_backward needs for these sizes and dtypes: the row vector
- * D = rowsum(dO * O) (float32 [B,H,N]) and, when in_dtype is FA_BF16, fp16 copies of Q, K, V and
- * dO (4 x [B,H,N,d] 16-bit) used as the MFMA operands. grad_dtype does not change the size but is
- * validated. Returns 0 for arguments fa_backward would reject.
+ * D = rowsum(dO * O) (float32 [B,H,N]), a per-head dO scale (float32 [B,H]), 256 partial maxima
+ * of |dO| per head, a flag word, the scaled fp16 copy of dO ([B,H,N,d] 16-bit) and, when in_dtype
+ * is FA_BF16, fp16 copies of Q, K and V (3 x [B,H,N,d] 16-bit) used as the MFMA operands.
+ * grad_dtype does not change the size but is validated. Returns 0 for arguments fa_backward would
+ * reject (e.g. an in_dtype / grad_dtype pair it does not provide).
  */
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d, fa_dtype in_dtype,
                                    fa_dtype grad_dtype);
+
+/*
+ * Input range of every backward entry point (fa_backward, fa_backward_kv, fa_backward_dropout,
+ * fa_backward_blocksparse). The five products run on fp16 MFMA operands with fp32 accumulation:
+ *   - Q, K and V: bf16 inputs are converted to fp16, which is exact for 2^-14 <= |x| <= 65504 and
+ *     changes smaller values by less than 2^-25. PRECONDITION: |Q|, |K|, |V| < 65520 elementwise
+ *     (larger bf16 values would become infinities). fp16 inputs are used as they are.
+ *   - dO: scaled per (b, h) by a power of two 2^s before its fp16 copy is taken, chosen from the
+ *     head's largest |dO| (s = 0 while that lies in [1/2, 16], so ordinary gradients keep their
+ *     bits; otherwise it is brought into [8, 16)). dP, D and dS scale along with it and stay
+ *     inside fp16's range for upstream gradients of any magnitude; the results are multiplied by
+ *     2^-s, which is exact. No precondition on dO beyond being finite.
+ * With FA_DEBUG_CHECKS=1 in the environment, a backward call with bf16 inputs first checks the
+ * precondition on the device, waits for the answer and returns FA_ERR_RANGE (launching no
+ * backward kernel) when it fails. The check needs no more workspace than the call itself.
+ */
 
 /*
  * Backward pass ("FlashAttention 为什么不需要存下注意力矩阵" §03 3.3; "FlashAttention V1 技术深度解析"
@@ -106,10 +127,10 @@ size_t fa_backward_workspace_bytes(int B, int H, int N, int d, fa_dtype in_dtype
  *   workspace  device buffer of at least fa_backward_workspace_bytes(B,H,N,d,in_dtype,grad_dtype)
  *              bytes,
  *              16-byte aligned; contents on entry are ignored and clobbered
- * Three kernels run on the stream: a row-wise preprocess (D, fp16 operand copies), a keys-outer
- * kernel for dK and dV, and a queries-outer kernel for dQ. Every product uses fp16 MFMA operands
- * with fp32 accumulation (bf16 inputs are converted exactly while |x| >= 2^-14). No atomics:
- * all outputs are deterministic.
+ * Four kernels run on the stream: a max pass (per-head max |dO|, fp16 copy of bf16 Q), a
+ * row-wise preprocess (dO scale, D, scaled fp16 dO), a keys-outer kernel for dK and dV, and a
+ * queries-outer kernel for dQ. Every product uses fp16 MFMA operands with fp32 accumulation
+ * (input range above). No atomics: all outputs are deterministic.
  */
 fa_status fa_backward(const void* q, const void* k, const void* v, const void* o,
                       const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
@@ -118,8 +139,9 @@ fa_status fa_backward(const void* q, const void* k, const void* v, const void* o
                       size_t workspace_bytes, void* stream);
 
 /*
- * Bytes of device workspace fa_backward_kv needs: D (float32 [B,H,Nq]) and, when in_dtype is
- * FA_BF16, fp16 copies of Q and dO ([B,H,Nq,d] each) and of K and V ([B,H,Nk,d] each). Equal to
+ * Bytes of device workspace fa_backward_kv needs: D (float32 [B,H,Nq]), the per-head dO scale and
+ * partial maxima, a flag word, the scaled fp16 copy of dO ([B,H,Nq,d]) and, when in_dtype is
+ * FA_BF16, fp16 copies of Q ([B,H,Nq,d]) and of K and V ([B,H,Nk,d] each). Equal to
  * fa_backward_workspace_bytes when Nq = Nk. Returns 0 for arguments fa_backward_kv would reject.
  */
 size_t fa_backward_kv_workspace_bytes(int B, int H, int Nq, int Nk, int d, fa_dtype in_dtype,

@@ -16,6 +16,20 @@ HEADER = os.path.join(ROOT, "include", "fa.h")
 P = 0x100000  # fake 16-byte-aligned device addresses (never dereferenced)
 
 
+def _r256(x):
+    return (x + 255) // 256 * 256
+
+
+def ws_expected(B_, H, nq, nk, d, bf16):
+    """Workspace bytes of the backward as include/fa.h documents them: D (fp32 [B,H,Nq]), the dO
+    scale (fp32 [B,H]), 256 partial maxima per head, a flag word, each section 256-byte aligned,
+    then the fp16 copies: dO always, Q, K and V for bf16 inputs."""
+    bh = B_ * H
+    head = _r256(4 * bh * nq) + _r256(4 * bh) + _r256(4 * 256 * bh) + 256
+    copies = bh * nq * d + ((bh * nq * d + 2 * bh * nk * d) if bf16 else 0)
+    return head + 2 * copies
+
+
 def _lib():
     if not os.path.exists(B.LIB_PATH):
         pytest.fail("libfa.so is not built (run python -m exact_attention_94_amd.build)")
@@ -39,10 +53,13 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = _lib()
-    for code in range(5):
+    names = ["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE",
+             "FA_ERR_HIP", "FA_ERR_RANGE"]
+    for code, name in enumerate(names):
         s = lib.fa_status_string(code).decode()
-        assert s.startswith(["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED",
-                             "FA_ERR_WORKSPACE", "FA_ERR_HIP"][code])
+        assert s.startswith(name)
+        assert getattr(B, name) == code
+        assert re.search(rf"\b{name}\s*=\s*{code}\b", open(HEADER, encoding="utf-8").read())
     assert "unknown" in lib.fa_status_string(99).decode()
 
 
@@ -103,8 +120,9 @@ def test_forward_rejects(kw, status):
     (dict(ws=P + 2), B.FA_ERR_WORKSPACE),
     (dict(ws_bytes=16), B.FA_ERR_WORKSPACE),
     (dict(g_dtype=B.FA_BF16, ws_bytes=2 * 3 * 100 * 4 + 256), B.FA_ERR_WORKSPACE),
-    (dict(in_dtype=B.FA_F16, o_dtype=B.FA_F32, ws_bytes=2559), B.FA_ERR_WORKSPACE),
-    (dict(ws_bytes=2560 + 4 * 2 * 3 * 100 * 64 * 2 - 1), B.FA_ERR_WORKSPACE),
+    (dict(in_dtype=B.FA_F16, o_dtype=B.FA_F32,
+          ws_bytes=ws_expected(2, 3, 100, 100, 64, False) - 1), B.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=ws_expected(2, 3, 100, 100, 64, True) - 1), B.FA_ERR_WORKSPACE),
 ])
 def test_backward_rejects(kw, status):
     assert bwd(**kw) == status
@@ -272,8 +290,7 @@ def bwd_kv(**kw):
     (dict(B=1, H=1, Nk=(1 << 24) + 1), B.FA_ERR_INVALID_ARG),
     (dict(ws=None), B.FA_ERR_WORKSPACE),
     # Q / dO copies over Nq rows, K / V copies over Nk rows: one byte short is rejected.
-    (dict(ws_bytes=2560 + (2 * 2 * 3 * 100 * 64 + 2 * 2 * 3 * 300 * 64) * 2 - 1),
-     B.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=ws_expected(2, 3, 100, 300, 64, True) - 1), B.FA_ERR_WORKSPACE),
 ])
 def test_backward_kv_rejects(kw, status):
     assert bwd_kv(**kw) == status
@@ -282,12 +299,10 @@ def test_backward_kv_rejects(kw, status):
 def test_backward_kv_workspace_bytes():
     lib = _lib()
     ws = lib.fa_backward_kv_workspace_bytes
-    assert ws(2, 3, 100, 300, 64, B.FA_F16, B.FA_F32) == 2560
-    assert ws(2, 3, 100, 300, 64, B.FA_BF16, B.FA_F32) == \
-        2560 + (2 * 2 * 3 * 100 * 64 + 2 * 2 * 3 * 300 * 64) * 2
+    assert ws(2, 3, 100, 300, 64, B.FA_F16, B.FA_F32) == ws_expected(2, 3, 100, 300, 64, False)
+    assert ws(2, 3, 100, 300, 64, B.FA_BF16, B.FA_F32) == ws_expected(2, 3, 100, 300, 64, True)
     # Non-causal calls may have more queries than keys.
-    assert ws(1, 1, 300, 17, 32, B.FA_BF16, B.FA_BF16) == \
-        round(300 * 4 / 256 + 0.5) * 256 + (2 * 300 * 32 + 2 * 17 * 32) * 2
+    assert ws(1, 1, 300, 17, 32, B.FA_BF16, B.FA_BF16) == ws_expected(1, 1, 300, 17, 32, True)
     for n in (1, 100, 4099):
         for dt in (B.FA_F16, B.FA_BF16):
             assert ws(2, 3, n, n, 96, dt, B.FA_F32) == \
@@ -295,26 +310,29 @@ def test_backward_kv_workspace_bytes():
     assert ws(1, 1, 10, 10, 256, B.FA_F16, B.FA_F32) == 0
     assert ws(1, 1, 10, 0, 64, B.FA_F16, B.FA_F32) == 0
     assert ws(1, 1, 10, 10, 64, B.FA_F16, 9) == 0
+    # Pairs fa_backward_kv rejects get 0, as the header promises.
+    assert ws(1, 1, 10, 20, 64, B.FA_BF16, B.FA_F16) == 0
 
 
 def test_workspace_bytes():
     lib = _lib()
     ws = lib.fa_backward_workspace_bytes
-    e = 2 * 3 * 100 * 64
-    # D vector rounded to 256 bytes; fp16 copies of Q, K, V, dO for bf16 inputs.
-    assert ws(2, 3, 100, 64, B.FA_F16, B.FA_F32) == 2560
-    assert ws(2, 3, 100, 64, B.FA_F16, B.FA_F16) == 2560
-    assert ws(2, 3, 100, 64, B.FA_BF16, B.FA_F32) == 2560 + 4 * e * 2
-    assert ws(2, 3, 100, 64, B.FA_BF16, B.FA_BF16) == 2560 + 4 * e * 2
-    assert ws(1, 1, 1, 128, B.FA_F16, B.FA_F16) == 256
+    assert ws(2, 3, 100, 64, B.FA_F16, B.FA_F32) == ws_expected(2, 3, 100, 100, 64, False)
+    assert ws(2, 3, 100, 64, B.FA_F16, B.FA_F16) == ws_expected(2, 3, 100, 100, 64, False)
+    assert ws(2, 3, 100, 64, B.FA_BF16, B.FA_F32) == ws_expected(2, 3, 100, 100, 64, True)
+    assert ws(2, 3, 100, 64, B.FA_BF16, B.FA_BF16) == ws_expected(2, 3, 100, 100, 64, True)
+    assert ws(1, 1, 1, 128, B.FA_F16, B.FA_F16) == ws_expected(1, 1, 1, 1, 128, False)
     assert ws(1, 1, 1, 80, B.FA_F16, B.FA_F32) == 0
     assert ws(1, 1, 1, 256, B.FA_F16, B.FA_F32) == 0  # no backward at d = 256
-    # Head dims 32 and 96 are provided; the workspace only depends on d through the copies.
-    assert ws(1, 1, 1, 96, B.FA_F16, B.FA_F32) == 256
-    assert ws(1, 2, 10, 32, B.FA_BF16, B.FA_F32) == 256 + 4 * 2 * 10 * 32 * 2
+    # Head dims 32 and 96 are provided; the workspace depends on d only through the copies.
+    assert ws(1, 1, 1, 96, B.FA_F16, B.FA_F32) == ws_expected(1, 1, 1, 1, 96, False)
+    assert ws(1, 2, 10, 32, B.FA_BF16, B.FA_F32) == ws_expected(1, 2, 10, 10, 32, True)
     assert ws(0, 1, 1, 64, B.FA_F16, B.FA_F32) == 0
     assert ws(1, 1, 1, 64, B.FA_F16, 9) == 0
     assert ws(1, 1, 1, 64, 9, B.FA_F32) == 0
+    # Every dtype pair fa_backward rejects gets 0: 16-bit gradients of the other 16-bit type.
+    assert ws(1, 1, 8, 64, B.FA_BF16, B.FA_F16) == 0
+    assert ws(1, 1, 8, 64, B.FA_F16, B.FA_BF16) == 0
 
 
 def test_exact_workspace_size_is_accepted_by_validation():
