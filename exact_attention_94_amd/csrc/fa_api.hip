@@ -58,8 +58,8 @@ bool make_drop(float p, uint64_t seed, uint32_t offset, fa::DropParams& dp) {
 
 // Workspace, each section 256-byte aligned: D (fp32 [B,H,Nq]) | the per-head dO scale 2^-s
 // (fp32 [B,H]) | partial maxima of |dO| (kMaxParts words per head) | a debug flag word |
-// fp16 copies: dO ([B,H,Nq,d]) always; for bf16 inputs also Q ([B,H,Nq,d]), K and V
-// ([B,H,Nk,d] each).
+// fp16 copies (16-bit inputs only): dO ([B,H,Nq,d]); for bf16 inputs also Q ([B,H,Nq,d]), K and
+// V ([B,H,Nk,d] each).
 struct WsLayout {
   size_t gscale_off, dmax_off, flag_off, f16_off, q_elems, k_elems, total;
 };
@@ -74,8 +74,9 @@ WsLayout workspace_layout(int B, int H, int Nq, int Nk, int d, fa_dtype in_dtype
   w.dmax_off = w.gscale_off + round_up(bh * sizeof(float), 256);
   w.flag_off = w.dmax_off + round_up(bh * fa::kMaxParts * sizeof(uint32_t), 256);
   w.f16_off = w.flag_off + 256;
-  const size_t f16_elems =
-      w.q_elems + ((in_dtype == FA_BF16) ? (w.q_elems + 2 * w.k_elems) : 0);
+  // fp32 inputs use their own tensors as operands: no copies.
+  const size_t f16_elems = in_dtype == FA_F32 ? 0
+                           : w.q_elems + ((in_dtype == FA_BF16) ? (w.q_elems + 2 * w.k_elems) : 0);
   w.total = w.f16_off + f16_elems * 2;
   return w;
 }
@@ -92,9 +93,11 @@ fa_status backward_dtypes_ok(int B, int H, int N, int Nk, int d, fa_dtype in_dty
     const fa_status sk = check_shape(B, H, Nk, d);
     if (sk != FA_OK) return sk;
   }
-  if (in_dtype == FA_F32 || d == 256) return FA_ERR_UNSUPPORTED;
+  if (d == 256) return FA_ERR_UNSUPPORTED;
   if (o_dtype != in_dtype && o_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
   if (grad_dtype != in_dtype && grad_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  // fp32 inputs: plain attention over N = Nk only (as the fp32 forward).
+  if (in_dtype == FA_F32 && (Nk != 0 || extra_mode)) return FA_ERR_UNSUPPORTED;
   if (Nk != 0 && extra_mode) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
@@ -272,8 +275,11 @@ fa_status backward_impl(const void* q, const void* k, const void* v, const void*
     a.sparse = *sparse;
     mode = fa::Mode::kSparse;
   }
-  const hipError_t e = fa::launch_backward(a, d, (int)in_dtype, (int)o_dtype, (int)grad_dtype,
-                                           causal != 0, mode, hs, t_prof_before, t_prof_after);
+  const hipError_t e =
+      in_dtype == FA_F32
+          ? fa::launch_backward_f32(a, d, causal != 0, hs)
+          : fa::launch_backward(a, d, (int)in_dtype, (int)o_dtype, (int)grad_dtype, causal != 0,
+                                mode, hs, t_prof_before, t_prof_after);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -108,6 +108,10 @@ hipError_t launch_backward(const BwdArgs& a, int d, int in_dtype, int o_dtype, i
                            bool causal, Mode mode, hipStream_t s, hipEvent_t ev_before,
                            hipEvent_t ev_after);
 
+// Backward of fp32 attention (in_dtype, o_dtype and grad_dtype all fp32; N = Nk): D, then the
+// keys-outer dK/dV and queries-outer dQ kernels on true-fp32 MFMA. Uses a.delta only.
+hipError_t launch_backward_f32(const BwdArgs& a, int d, bool causal, hipStream_t s);
+
 // Debug range check of 16-bit inputs bound for fp16 operands: sets *flag to 1 if any of the n
 // 16-bit bf16 values at x has a magnitude fp16 cannot hold (|x| >= 65536 after rounding, or not
 // finite). *flag must be zero beforehand (clear_flag).

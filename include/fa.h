@@ -24,7 +24,8 @@
  * B, H >= 1 with B*H*N*d < 2^31
  * and N*d <= 2^30;
  * in_dtype in {FA_F32, FA_F16, FA_BF16}; any finite scale; causal in {0, 1}.
- * The backward supports in_dtype FA_F16 and FA_BF16.
+ * The backward supports all three input dtypes (fp32 inputs: O and the gradients in fp32, N = Nk,
+ * no dropout or block mask, as the fp32 forward).
  *
  * Ownership: the caller owns every buffer and the stream. The library never allocates or frees
  * device memory; the backward takes a caller-provided workspace.
@@ -119,7 +120,7 @@ size_t fa_backward_workspace_bytes(int B, int H, int N, int d, fa_dtype in_dtype
  * Backward pass ("FlashAttention 为什么不需要存下注意力矩阵" §03 3.3; "FlashAttention V1 技术深度解析"
  * §4.2: recompute each P tile from the saved statistics instead of storing P).
  *
- *   q, k, v    [B,H,N,d] in in_dtype (FA_F16 or FA_BF16), the forward's inputs
+ *   q, k, v    [B,H,N,d] in in_dtype (FA_F32, FA_F16 or FA_BF16), the forward's inputs
  *   o          [B,H,N,d] in o_dtype (in_dtype or FA_F32), the forward's output
  *   dout       [B,H,N,d] in in_dtype, the upstream gradient dL/dO
  *   lse        [B,H,N] float32, the forward's logsumexp
@@ -130,7 +131,8 @@ size_t fa_backward_workspace_bytes(int B, int H, int N, int d, fa_dtype in_dtype
  * Four kernels run on the stream: a max pass (per-head max |dO|, fp16 copy of bf16 Q), a
  * row-wise preprocess (dO scale, D, scaled fp16 dO), a keys-outer kernel for dK and dV, and a
  * queries-outer kernel for dQ. Every product uses fp16 MFMA operands with fp32 accumulation
- * (input range above). No atomics: all outputs are deterministic.
+ * (input range above). fp32 inputs instead run three kernels (D, dK/dV, dQ) on true-fp32 MFMA
+ * with no operand copies and no scaling. No atomics: all outputs are deterministic.
  */
 fa_status fa_backward(const void* q, const void* k, const void* v, const void* o,
                       const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,

@@ -20,13 +20,14 @@ def _r256(x):
     return (x + 255) // 256 * 256
 
 
-def ws_expected(B_, H, nq, nk, d, bf16):
+def ws_expected(B_, H, nq, nk, d, bf16, f32=False):
     """Workspace bytes of the backward as include/fa.h documents them: D (fp32 [B,H,Nq]), the dO
     scale (fp32 [B,H]), 256 partial maxima per head, a flag word, each section 256-byte aligned,
-    then the fp16 copies: dO always, Q, K and V for bf16 inputs."""
+    then the fp16 copies of 16-bit inputs: dO always, Q, K and V for bf16 inputs (fp32 inputs:
+    none)."""
     bh = B_ * H
     head = _r256(4 * bh * nq) + _r256(4 * bh) + _r256(4 * 256 * bh) + 256
-    copies = bh * nq * d + ((bh * nq * d + 2 * bh * nk * d) if bf16 else 0)
+    copies = 0 if f32 else bh * nq * d + ((bh * nq * d + 2 * bh * nk * d) if bf16 else 0)
     return head + 2 * copies
 
 
@@ -113,7 +114,13 @@ def test_forward_rejects(kw, status):
     (dict(causal=-1), B.FA_ERR_INVALID_ARG),
     (dict(g_dtype=5), B.FA_ERR_INVALID_ARG),
     (dict(d=256), B.FA_ERR_UNSUPPORTED),
-    (dict(in_dtype=B.FA_F32, o_dtype=B.FA_F32), B.FA_ERR_UNSUPPORTED),
+    (dict(d=256, in_dtype=B.FA_F32, o_dtype=B.FA_F32), B.FA_ERR_UNSUPPORTED),
+    (dict(in_dtype=B.FA_F32, o_dtype=B.FA_F32, g_dtype=B.FA_F16), B.FA_ERR_UNSUPPORTED),
+    (dict(in_dtype=B.FA_F32, o_dtype=B.FA_BF16), B.FA_ERR_UNSUPPORTED),
+    # fp32 inputs pass the dtype checks and reach the workspace check.
+    (dict(in_dtype=B.FA_F32, o_dtype=B.FA_F32, ws=None), B.FA_ERR_WORKSPACE),
+    (dict(in_dtype=B.FA_F32, o_dtype=B.FA_F32,
+          ws_bytes=ws_expected(2, 3, 100, 100, 64, False, f32=True) - 1), B.FA_ERR_WORKSPACE),
     (dict(g_dtype=B.FA_F16), B.FA_ERR_UNSUPPORTED),
     (dict(o_dtype=B.FA_F16), B.FA_ERR_UNSUPPORTED),
     (dict(ws=None), B.FA_ERR_WORKSPACE),
@@ -333,6 +340,10 @@ def test_workspace_bytes():
     # Every dtype pair fa_backward rejects gets 0: 16-bit gradients of the other 16-bit type.
     assert ws(1, 1, 8, 64, B.FA_BF16, B.FA_F16) == 0
     assert ws(1, 1, 8, 64, B.FA_F16, B.FA_BF16) == 0
+    assert ws(1, 1, 8, 64, B.FA_F32, B.FA_F16) == 0
+    assert ws(1, 1, 8, 64, B.FA_F32, B.FA_BF16) == 0
+    # fp32 inputs need no operand copies.
+    assert ws(2, 3, 100, 64, B.FA_F32, B.FA_F32) == ws_expected(2, 3, 100, 100, 64, False, True)
 
 
 def test_exact_workspace_size_is_accepted_by_validation():
@@ -370,3 +381,4 @@ def test_profile_hook_argument_check():
     assert lib.fa_profile_backward_main(P, None) == B.FA_ERR_INVALID_ARG
     assert lib.fa_profile_backward_main(None, P) == B.FA_ERR_INVALID_ARG
     assert lib.fa_profile_backward_main(None, None) == B.FA_OK
+
