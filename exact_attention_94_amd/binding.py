@@ -21,8 +21,10 @@ FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 EXPORTS = ("fa_forward", "fa_forward_dropout", "fa_forward_blocksparse", "fa_forward_kv",
            "fa_backward", "fa_backward_kv", "fa_backward_kv_workspace_bytes",
            "fa_backward_dropout", "fa_backward_blocksparse", "fa_backward_workspace_bytes",
-           "fa_decode_workspace_bytes", "fa_decode_forward", "fa_profile_backward_main",
-           "fa_status_string")
+           "fa_decode_workspace_bytes", "fa_decode_forward", "fa_decode_forward_noalloc",
+           "fa_profile_backward_main", "fa_status_string")
+
+DECODE_SCRATCH_BYTES = 8 << 20  # FA_DECODE_SCRATCH_BYTES
 
 SPARSE_BLOCK = 128  # queries x keys covered by one block-mask byte (FA_SPARSE_BLOCK)
 
@@ -79,6 +81,8 @@ def load(path=LIB_PATH):
     lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_decode_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
     lib.fa_decode_forward.restype = i
+    lib.fa_decode_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp]
+    lib.fa_decode_forward_noalloc.restype = i
     lib.fa_profile_backward_main.argtypes = [vp, vp]
     lib.fa_profile_backward_main.restype = i
     lib.fa_status_string.argtypes = [i]
@@ -273,11 +277,14 @@ def decode_workspace_bytes(B, H, Nq, Nk, d):
     return int(load().fa_decode_workspace_bytes(B, H, Nq, Nk, d))
 
 
-def decode(q, k, v, scale=None, causal=False, o_dtype=None, out=None, lse=None, workspace=None):
+def decode(q, k, v, scale=None, causal=False, o_dtype=None, out=None, lse=None, workspace=None,
+           no_alloc=False):
     """fa_decode_forward: q [B, H, Nq, d] (Nq <= 4) against k, v [B, H, Nk, d]. Returns (O, LSE).
 
     The queries are the last Nq positions of the sequence (causal: query i sees keys
-    0 .. Nk - Nq + i). `workspace` (a uint8 GPU tensor) is allocated when not given.
+    0 .. Nk - Nq + i). `workspace` (a uint8 GPU tensor) is allocated when not given. With
+    no_alloc=True the call is fa_decode_forward_noalloc, whose partials live in the library's own
+    device scratch (no workspace; give `out` and `lse` to make the whole call allocation-free).
     """
     torch = _torch()
     _check_bhnd("q", q)
@@ -297,6 +304,14 @@ def decode(q, k, v, scale=None, causal=False, o_dtype=None, out=None, lse=None, 
         _check_bhnd("out", out, q.shape)
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if no_alloc:
+        st = load().fa_decode_forward_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                              out.data_ptr(), lse.data_ptr(), B, H, Nq, Nk, d,
+                                              scale, int(bool(causal)), dtype_code(q.dtype),
+                                              dtype_code(out.dtype), _stream(q))
+        if st != FA_OK:
+            raise FAError(st, "fa_decode_forward_noalloc")
+        return out, lse
     need = decode_workspace_bytes(B, H, Nq, Nk, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)

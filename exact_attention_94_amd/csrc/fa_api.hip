@@ -11,6 +11,7 @@
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+static_assert(FA_DECODE_SCRATCH_BYTES == fa::kDecodeScratchBytes, "scratch size mismatch");
 
 bool valid_dtype(int t) { return t == FA_F32 || t == FA_F16 || t == FA_BF16; }
 
@@ -456,6 +457,28 @@ fa_status fa_decode_forward(const void* q, const void* k, const void* v, void* o
   const hipError_t e = fa::launch_decode(a, d, (int)in_dtype, o_dtype == FA_F32, causal != 0,
                                          static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_decode_forward_noalloc(const void* q, const void* k, const void* v, void* o,
+                                    float* lse, int B, int H, int Nq, int Nk, int d, float scale,
+                                    int causal, fa_dtype in_dtype, fa_dtype o_dtype,
+                                    void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_INVALID_ARG;
+  if (!valid_dtype(in_dtype) || !valid_dtype(o_dtype)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+  DecLayout L;
+  const fa_status st = decode_layout(B, H, Nq, Nk, d, L);
+  if (st != FA_OK) return st;
+  if (in_dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if (o_dtype != in_dtype && o_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if (L.total > fa::kDecodeScratchBytes) return FA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (fa::decode_scratch(&ws) != hipSuccess) return FA_ERR_HIP;
+  return fa_decode_forward(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, in_dtype, o_dtype,
+                           ws, L.total, stream);
 }
 
 fa_status fa_profile_backward_main(void* before, void* after) {

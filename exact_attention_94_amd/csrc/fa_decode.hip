@@ -17,6 +17,8 @@
 // across the workgroup's waves through LDS. K and V are read with the non-temporal (streaming)
 // cache policy: each byte is used once, so keeping it in the caches only evicts other data
 // (measured: 5.7 -> 6.5 TB/s on a 1 GB bf16 cache).
+#include <mutex>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -307,6 +309,37 @@ hipError_t launch_decode(const DecArgs& a, int d, int in_dtype, bool o_f32, bool
   const bool bf = in_dtype == 2;
   return d == 64 ? launch_dec_d<64>(a, bf, causal, o_f32, s)
                  : launch_dec_d<128>(a, bf, causal, o_f32, s);
+}
+
+// ----------------------------------------------------------------------------------------
+// Scratch for the allocation-free decoding entry point: the per-chunk partials live in this
+// file-scope device array instead of a caller workspace. Each GPU the library runs on holds its
+// own copy until the process ends. In host code `scratch` names a host-side stand-in, not a
+// device address, so the kernels only ever receive the address hipGetSymbolAddress reports for
+// the current device, fetched once per device and kept below.
+// ----------------------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace fa

@@ -92,6 +92,12 @@ struct DecArgs {
 // Upper bound of the number of key chunks per head (the merge kernel keeps their weights in LDS).
 constexpr int kDecodeMaxSplit = 2048;
 
+// Bytes of the device-resident scratch array of the allocation-free decoding entry point
+// (FA_DECODE_SCRATCH_BYTES in fa.h), and its address on the current device (looked up once per
+// device with hipGetSymbolAddress; never the host-side name of the array).
+constexpr size_t kDecodeScratchBytes = (size_t)8 << 20;
+hipError_t decode_scratch(void** out);
+
 // Chunking of Nk keys for bh heads (shared by the workspace size query and the launch).
 void decode_plan(int bh, int nk, int d, int& n_split, int& chunk);
 hipError_t launch_decode(const DecArgs& a, int d, int in_dtype, bool o_f32, bool causal,

@@ -261,6 +261,27 @@ fa_status fa_decode_forward(const void* q, const void* k, const void* v, void* o
                             fa_dtype in_dtype, fa_dtype o_dtype, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/* Bytes of device scratch that fa_decode_forward_noalloc has on each GPU. */
+#define FA_DECODE_SCRATCH_BYTES (8u << 20)
+
+/*
+ * fa_decode_forward without a workspace, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation. Same arguments
+ * (minus the workspace), computation, kernels and results as fa_decode_forward. The per-chunk
+ * partials live in a device array of FA_DECODE_SCRATCH_BYTES that the library holds on each GPU
+ * it runs on until the process ends; the call itself allocates nothing (no hipMalloc, no
+ * allocating library routine). Calls needing more scratch than that, i.e. with
+ * fa_decode_workspace_bytes(B, H, Nq, Nk, d) > FA_DECODE_SCRATCH_BYTES, return FA_ERR_WORKSPACE
+ * before any launch. Every call on one GPU uses that GPU's single array: calls that may overlap
+ * in time on one GPU (different streams, different threads) race on it and must be serialised
+ * by the caller. Nothing needs clearing between calls (every partial is written before it is
+ * read). Other errors as fa_decode_forward.
+ */
+fa_status fa_decode_forward_noalloc(const void* q, const void* k, const void* v, void* o,
+                                    float* lse, int B, int H, int Nq, int Nk, int d, float scale,
+                                    int causal, fa_dtype in_dtype, fa_dtype o_dtype,
+                                    void* stream);
+
 /*
  * Profiling aid with no effect on results: after this call, every fa_backward call made by the
  * calling thread records `before` on its stream immediately before its dK/dV kernel (the

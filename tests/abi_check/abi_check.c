@@ -181,6 +181,17 @@ int main(void) {
                            NULL),
          FA_ERR_UNSUPPORTED);
 
+  /* Allocation-free decoding: validation, and calls too large for its scratch. */
+  EXPECT(fa_decode_forward_noalloc(NULL, P, P, P, FP, 1, 1, 1, 100, 64, 0.1f, 1, FA_BF16,
+                                   FA_BF16, NULL),
+         FA_ERR_INVALID_ARG);
+  EXPECT(fa_decode_forward_noalloc(P, P, P, P, FP, 64, 128, 4, 256, 128, 0.1f, 1, FA_BF16,
+                                   FA_BF16, NULL),
+         FA_ERR_WORKSPACE);
+  EXPECT(fa_decode_forward_noalloc(P, P, P, P, FP, INT_MAX, 128, 4, 256, 128, 0.1f, 1, FA_BF16,
+                                   FA_BF16, NULL),
+         FA_ERR_INVALID_ARG);
+
   /* Profiling hook. */
   EXPECT(fa_profile_backward_main(P, NULL), FA_ERR_INVALID_ARG);
   EXPECT(fa_profile_backward_main(NULL, NULL), FA_OK);

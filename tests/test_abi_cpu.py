@@ -382,3 +382,29 @@ def test_profile_hook_argument_check():
     assert lib.fa_profile_backward_main(None, P) == B.FA_ERR_INVALID_ARG
     assert lib.fa_profile_backward_main(None, None) == B.FA_OK
 
+
+def test_decode_noalloc_rejects():
+    """The allocation-free decoding entry point validates like fa_decode_forward and refuses calls
+    whose partials would not fit its fixed device scratch, before any HIP call."""
+    lib = _lib()
+    f = lib.fa_decode_forward_noalloc
+
+    def call(**kw):
+        a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, Nq=1, Nk=100, d=64, scale=0.125, causal=1,
+                 in_dtype=B.FA_BF16, o_dtype=B.FA_BF16)
+        a.update(kw)
+        return f(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"], a["Nk"],
+                 a["d"], a["scale"], a["causal"], a["in_dtype"], a["o_dtype"], None)
+
+    assert call(q=None) == B.FA_ERR_INVALID_ARG
+    assert call(lse=P + 4) == B.FA_ERR_INVALID_ARG
+    assert call(Nq=5) == B.FA_ERR_UNSUPPORTED
+    assert call(Nq=3, Nk=2) == B.FA_ERR_INVALID_ARG
+    assert call(d=32) == B.FA_ERR_UNSUPPORTED
+    assert call(in_dtype=B.FA_F32, o_dtype=B.FA_F32) == B.FA_ERR_UNSUPPORTED
+    assert call(scale=float("inf")) == B.FA_ERR_INVALID_ARG
+    big = dict(B=64, H=128, Nq=4, Nk=256, d=128)
+    assert lib.fa_decode_workspace_bytes(64, 128, 4, 256, 128) > B.DECODE_SCRATCH_BYTES
+    assert call(**big) == B.FA_ERR_WORKSPACE
+    assert re.search(r"#define\s+FA_DECODE_SCRATCH_BYTES\s+\(8u\s*<<\s*20\)",
+                     open(HEADER, encoding="utf-8").read())
