@@ -94,7 +94,8 @@ fa_status backward_dtypes_ok(int B, int H, int N, int Nk, int d, fa_dtype in_dty
     const fa_status sk = check_shape(B, H, Nk, d);
     if (sk != FA_OK) return sk;
   }
-  if (d == 256) return FA_ERR_UNSUPPORTED;
+  // d = 256: plain 16-bit attention only (as the forward).
+  if (d == 256 && (in_dtype == FA_F32 || extra_mode)) return FA_ERR_UNSUPPORTED;
   if (o_dtype != in_dtype && o_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
   if (grad_dtype != in_dtype && grad_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
   // fp32 inputs: plain attention over N = Nk only (as the fp32 forward).

@@ -61,7 +61,7 @@ __device__ __forceinline__ u32x4 to_f16x8(u32x4 v) {
 // row sum is a butterfly over them; the extra threads of d = 96 contribute zero).
 template <int D>
 constexpr int pre_tpr() {
-  return D <= 32 ? 4 : D <= 64 ? 8 : 16;
+  return D <= 32 ? 4 : D <= 64 ? 8 : D <= 128 ? 16 : 32;
 }
 
 // Largest value of x over the workgroup (256 threads), returned to every thread.
@@ -239,7 +239,9 @@ template <int D>
 struct Dkdv {
   static constexpr int NT = 256;       // 4 waves
   static constexpr int BKV = 128;      // keys per workgroup (32 per wave)
-  static constexpr int BQ = 64;        // queries per step
+  // Queries per step: 64, or 32 at d = 256, where dK and dV alone fill 256 accumulator
+  // registers and K and V another 128 (one wave per SIMD, the whole register file).
+  static constexpr int BQ = D >= 256 ? 32 : 64;
   static constexpr int QBS = BQ / 32;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
@@ -382,8 +384,10 @@ __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs 
     if (wave == 0) {
       // Rows beyond N, and rows that saw no key (LSE = -inf, block-sparse only), get +inf, so
       // that P = 0 there.
-      vec[lane] = (i0 + lane < N && lreg != -INFINITY) ? lreg * kLog2e : INFINITY;
-      vec[C::BQ + lane] = dreg;
+      if (lane < C::BQ) {
+        vec[lane] = (i0 + lane < N && lreg != -INFINITY) ? lreg * kLog2e : INFINITY;
+        vec[C::BQ + lane] = dreg;
+      }
     }
   };
 
@@ -555,14 +559,18 @@ struct Dq {
   static constexpr int NT = 256;   // 4 waves x 32 queries
   static constexpr int NW = 4;
   static constexpr int BR = 128;   // queries per workgroup
-  static constexpr int BC = 64;    // keys per K/V tile
+  // Keys per K/V tile: 64, or 32 at d = 256 (fewer score registers next to the 256-wide Q, dO
+  // and dQ fragments).
+  static constexpr int BC = D >= 256 ? 32 : 64;
+  static constexpr int KB = BC / 32;  // 32-key MFMA blocks per tile
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int TILE = BC * D;     // swizzled rows, no padding
   static constexpr int STAGE = 2 * TILE;  // K then V
   static constexpr int LDS_BYTES = 2 * STAGE * 2;
   static constexpr int LD_INSTR = BC * D * 2 / 1024;  // 1 KB direct loads per tile and tensor
-  static constexpr int MIN_WG = (D <= 64) ? kDqWaves64 : 2;
+  // Waves per SIMD the register allocation must allow (d = 256: one, the whole file).
+  static constexpr int MIN_WG = (D <= 64) ? kDqWaves64 : D <= 128 ? 2 : 1;
 };
 
 template <int D, bool IS_BF16, bool G_F32, bool CAUSAL, bool DROP, bool SPARSE>
@@ -671,23 +679,23 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
     const uint16_t* ks_ = smem + stage * C::STAGE;
     const uint16_t* vs_ = ks_ + C::TILE;
     // S^T = K Q^T and dP^T = V dO^T: rows = keys (permuted), column = this lane's query.
-    f32x16 sacc[2], pacc[2];
+    f32x16 sacc[C::KB], pacc[C::KB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         sacc[kb][i] = 0.f;
         pacc[kb][i] = 0.f;
       }
     // Fragment f = (ks, kb, tensor: K for S^T, V for dP^T), read dq_pre<D>() ahead of its MFMA.
-    read_ahead<2 * C::KS * 2, dq_pre<D>()>(
+    read_ahead<2 * C::KS * C::KB, dq_pre<D>()>(
         [&](int f) {
-          const int ks = f / 4, kb = (f / 2) % 2;
+          const int ks = f / (2 * C::KB), kb = (f / 2) % C::KB;
           const uint16_t* src = (f & 1) ? vs_ : ks_;
           return *reinterpret_cast<const u32x4*>(src + swz_off<D>(kb * 32 + r, ks * 16 + g * 8));
         },
         [&](int f, const Frag16& fr) {
-          const int ks = f / 4, kb = (f / 2) % 2;
+          const int ks = f / (2 * C::KB), kb = (f / 2) % C::KB;
           if (f & 1) pacc[kb] = mfma32x32x16<false>(fr, of[ks], pacc[kb]);
           else sacc[kb] = mfma32x32x16<false>(fr, qf[ks], sacc[kb]);
         });
@@ -695,7 +703,7 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
     // j0 + 32*kb + 16*(i/8) + 8*g + i%8.
     if ((j0 + C::BC > Nk) || (CAUSAL && (j0 + C::BC - 1 > qw0 + qoff))) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int kk = j0 + kb * 32 + (i >> 3) * 16 + g * 8 + (i & 7);
@@ -705,9 +713,9 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
     }
     // dS^T = P^T * (dP^T - D), P = exp2(c*S - LSE*log2e); with dropout dP is (dO V^T) * keep /
     // keep rate, the keep bits of this lane's 8 keys coming from one Philox block.
-    Frag16 dsf[2][2];
+    Frag16 dsf[C::KB][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         uint32_t bits = 0xFFu;
@@ -732,7 +740,7 @@ __global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
     // dQ^T += K^T dS^T: A = K read transposed (keys 32kb + 16h + 8g + s sit on staged rows
     // 32kb + 16h + 4g + s and + 8), B = dS^T slots.
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int row = kb * 32 + h * 16 + g * 4;
@@ -859,6 +867,16 @@ static hipError_t launch_all(const BwdArgs& a, bool o_f32, bool g_f32, bool caus
                : launch_grads_m<D, IS_BF16, false>(a, causal, drop, s, ev_before, ev_after);
 }
 
+template <int D, bool IS_BF16>
+static hipError_t launch_all_plain(const BwdArgs& a, bool o_f32, bool g_f32, bool causal,
+                                   hipStream_t s, hipEvent_t ev_before, hipEvent_t ev_after) {
+  hipError_t e = launch_pre<D, IS_BF16>(a, o_f32, s);
+  if (e != hipSuccess) return e;
+  return g_f32 ? launch_grads_c<D, IS_BF16, true, false, false>(a, causal, s, ev_before, ev_after)
+               : launch_grads_c<D, IS_BF16, false, false, false>(a, causal, s, ev_before,
+                                                                  ev_after);
+}
+
 hipError_t launch_backward(const BwdArgs& a, int d, int in_dtype, int o_dtype, int grad_dtype,
                            bool causal, Mode drop, hipStream_t s, hipEvent_t ev_before,
                            hipEvent_t ev_after) {
@@ -875,9 +893,13 @@ hipError_t launch_backward(const BwdArgs& a, int d, int in_dtype, int o_dtype, i
     case 96:
       return bf ? launch_all<96, true>(a, o_f32, g_f32, causal, drop, s, ev_before, ev_after)
                 : launch_all<96, false>(a, o_f32, g_f32, causal, drop, s, ev_before, ev_after);
-    default:
+    case 128:
       return bf ? launch_all<128, true>(a, o_f32, g_f32, causal, drop, s, ev_before, ev_after)
                 : launch_all<128, false>(a, o_f32, g_f32, causal, drop, s, ev_before, ev_after);
+    default:  // d = 256: plain attention only (the C ABI rejects dropout and block masks here)
+      if (drop != Mode::kPlain) return hipErrorInvalidValue;
+      return bf ? launch_all_plain<256, true>(a, o_f32, g_f32, causal, s, ev_before, ev_after)
+                : launch_all_plain<256, false>(a, o_f32, g_f32, causal, s, ev_before, ev_after);
   }
 }
 

@@ -116,8 +116,10 @@ int main(void) {
   EXPECT(bwd(P, P, 2, 3, 100, 64, nan, 1, FA_BF16, FA_F32, FA_F32, P, big), FA_ERR_INVALID_ARG);
   EXPECT(bwd(P, P, 2, 3, 100, 64, 0.1f, 1, FA_BF16, FA_F32, 9, P, big), FA_ERR_INVALID_ARG);
   EXPECT(bwd(P, P, 2, 3, 100, 64, 0.1f, 1, FA_BF16, FA_F32, FA_F16, P, big), FA_ERR_UNSUPPORTED);
-  EXPECT(bwd(P, P, 2, 3, 100, 256, 0.1f, 1, FA_BF16, FA_F32, FA_F32, P, big),
+  EXPECT(bwd(P, P, 2, 3, 100, 256, 0.1f, 1, FA_F32, FA_F32, FA_F32, P, big),
          FA_ERR_UNSUPPORTED);
+  EXPECT(bwd(P, P, 2, 3, 100, 256, 0.1f, 1, FA_BF16, FA_F32, FA_F32, NULL, big),
+         FA_ERR_WORKSPACE);
   EXPECT(bwd(P, P, 2, 3, 100, 64, 0.1f, 1, FA_BF16, FA_F32, FA_F32, NULL, big),
          FA_ERR_WORKSPACE);
   EXPECT(bwd(P, P, 2, 3, 100, 64, 0.1f, 1, FA_BF16, FA_F32, FA_F32, PM, big), FA_ERR_WORKSPACE);

@@ -113,8 +113,9 @@ def test_forward_rejects(kw, status):
     (dict(scale=float("nan")), B.FA_ERR_INVALID_ARG),
     (dict(causal=-1), B.FA_ERR_INVALID_ARG),
     (dict(g_dtype=5), B.FA_ERR_INVALID_ARG),
-    (dict(d=256), B.FA_ERR_UNSUPPORTED),
     (dict(d=256, in_dtype=B.FA_F32, o_dtype=B.FA_F32), B.FA_ERR_UNSUPPORTED),
+    # d = 256 (16-bit) passes the checks and reaches the workspace check.
+    (dict(d=256, ws=None), B.FA_ERR_WORKSPACE),
     (dict(in_dtype=B.FA_F32, o_dtype=B.FA_F32, g_dtype=B.FA_F16), B.FA_ERR_UNSUPPORTED),
     (dict(in_dtype=B.FA_F32, o_dtype=B.FA_BF16), B.FA_ERR_UNSUPPORTED),
     # fp32 inputs pass the dtype checks and reach the workspace check.
@@ -292,7 +293,7 @@ def bwd_kv(**kw):
     (dict(dk=None), B.FA_ERR_INVALID_ARG),
     (dict(dv=P + 4), B.FA_ERR_INVALID_ARG),
     (dict(in_dtype=B.FA_F32, o_dtype=B.FA_F32), B.FA_ERR_UNSUPPORTED),
-    (dict(d=256), B.FA_ERR_UNSUPPORTED),
+    (dict(d=256, ws=None), B.FA_ERR_WORKSPACE),  # d = 256 is provided (16-bit)
     (dict(d=80), B.FA_ERR_UNSUPPORTED),
     (dict(B=1, H=1, Nk=(1 << 24) + 1), B.FA_ERR_INVALID_ARG),
     (dict(ws=None), B.FA_ERR_WORKSPACE),
@@ -314,7 +315,7 @@ def test_backward_kv_workspace_bytes():
         for dt in (B.FA_F16, B.FA_BF16):
             assert ws(2, 3, n, n, 96, dt, B.FA_F32) == \
                 lib.fa_backward_workspace_bytes(2, 3, n, 96, dt, B.FA_F32)
-    assert ws(1, 1, 10, 10, 256, B.FA_F16, B.FA_F32) == 0
+    assert ws(1, 1, 10, 10, 256, B.FA_F16, B.FA_F32) == ws_expected(1, 1, 10, 10, 256, False)
     assert ws(1, 1, 10, 0, 64, B.FA_F16, B.FA_F32) == 0
     assert ws(1, 1, 10, 10, 64, B.FA_F16, 9) == 0
     # Pairs fa_backward_kv rejects get 0, as the header promises.
@@ -330,7 +331,8 @@ def test_workspace_bytes():
     assert ws(2, 3, 100, 64, B.FA_BF16, B.FA_BF16) == ws_expected(2, 3, 100, 100, 64, True)
     assert ws(1, 1, 1, 128, B.FA_F16, B.FA_F16) == ws_expected(1, 1, 1, 1, 128, False)
     assert ws(1, 1, 1, 80, B.FA_F16, B.FA_F32) == 0
-    assert ws(1, 1, 1, 256, B.FA_F16, B.FA_F32) == 0  # no backward at d = 256
+    assert ws(1, 1, 1, 256, B.FA_F16, B.FA_F32) == ws_expected(1, 1, 1, 1, 256, False)
+    assert ws(1, 1, 1, 256, B.FA_F32, B.FA_F32) == 0  # no fp32 attention at d = 256
     # Head dims 32 and 96 are provided; the workspace depends on d only through the copies.
     assert ws(1, 1, 1, 96, B.FA_F16, B.FA_F32) == ws_expected(1, 1, 1, 1, 96, False)
     assert ws(1, 2, 10, 32, B.FA_BF16, B.FA_F32) == ws_expected(1, 2, 10, 10, 32, True)

@@ -91,7 +91,7 @@ def test_forward_kv_is_the_tail_of_the_full_causal_forward(fa):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("d", [32, 64, 96, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_backward_kv_sweep(fa, dtype, d, causal):
     import torch

@@ -196,6 +196,56 @@ def test_backward_sweep(fa, dtype, d, causal):
             check("dV", host64(dv), g["dv"], 2e-2)
 
 
+# d = 256 (16-bit): one wave per SIMD, the register file holding dK/dV or Q, dO and dQ; ragged
+# sweeps, then a full-chip grid with every output checked finite and sampled heads compared.
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_sweep_d256(fa, dtype, causal):
+    import torch
+    d = 256
+    for n in [1, 17, 31, 32, 33, 64, 65, 129, 300]:
+        for (B, H) in ((1, 2), (2, 3)):
+            print(f"  N={n} B={B} H={H}", flush=True)
+            t = inp.draw((B, H, n, d), dtype, n * 11 + d, with_do=True)
+            scale = 1.0 / math.sqrt(d)
+            q, k, v, out, lse = _run_fwd(fa, t, causal, scale, o_dtype=torch.float32)
+            do = to_device(t["do"])
+            grads = tuple(nan_like(q.shape, torch.float32) for _ in range(3))
+            dq, dk, dv = fa.backward(q, k, v, out, do, lse, scale=scale, causal=causal,
+                                     grad_dtype=torch.float32, grads=grads)
+            torch.cuda.synchronize()
+            g = attn_bwd_ref(t["q"].values, t["k"].values, t["v"].values, t["do"].values, scale,
+                             causal)
+            check("dQ", host64(dq), g["dq"], 2e-2)
+            check("dK", host64(dk), g["dk"], 2e-2)
+            check("dV", host64(dv), g["dv"], 2e-2)
+
+
+@pytest.mark.parametrize("g_f32", [True, False])
+def test_backward_d256_full_grid(fa, g_f32):
+    import torch
+    B, H, n, d = 2, 16, 1000, 256
+    t = inp.draw((B, H, n, d), "bf16", 7256, with_do=True)
+    scale = 1.0 / math.sqrt(d)
+    q, k, v, out, lse = _run_fwd(fa, t, True, scale, o_dtype=torch.float32)
+    do = to_device(t["do"])
+    gd = torch.float32 if g_f32 else q.dtype
+    grads = tuple(nan_like(q.shape, gd) for _ in range(3))
+    dq, dk, dv = fa.backward(q, k, v, out, do, lse, scale=scale, causal=True, grad_dtype=gd,
+                             grads=grads)
+    torch.cuda.synchronize()
+    for x in (dq, dk, dv):
+        assert torch.isfinite(x).all(), "unwritten gradient rows"
+    for (b, h) in _xcd_spread(B, H):
+        print(f"  head (b={b}, h={h})", flush=True)
+        sel = lambda x: x[b, h]  # noqa: E731
+        g = attn_bwd_ref(sel(t["q"].values), sel(t["k"].values), sel(t["v"].values),
+                         sel(t["do"].values), scale, True)
+        check("dQ", host64(dq[b, h]), g["dq"], 2e-2)
+        check("dK", host64(dk[b, h]), g["dk"], 2e-2)
+        check("dV", host64(dv[b, h]), g["dv"], 2e-2)
+
+
 # fp32 inputs: true-fp32 MFMA throughout, gradients within the fp32 tolerance of 1e-5.
 @pytest.mark.parametrize("d", [32, 64, 96, 128])
 @pytest.mark.parametrize("causal", [False, True])
