@@ -235,13 +235,25 @@ __device__ __forceinline__ void store_grad4(void* base, size_t off, float x0, fl
 // ----------------------------------------------------------------------------------------
 // 2. dK / dV: keys outer.
 // ----------------------------------------------------------------------------------------
-template <int D>
+// Queries per step of the keys-outer kernel and keys per tile of the queries-outer kernel: from
+// the tuning table for plain attention and dropout, 64 for block-sparse masks (half a mask
+// block).
+template <int D, bool IS_BF16, bool CAUSAL, bool SPARSE>
+constexpr int dkdv_bq() {
+  return SPARSE ? 64 : dkdv_step_queries<D, IS_BF16, CAUSAL>();
+}
+template <int D, bool IS_BF16, bool CAUSAL, bool SPARSE>
+constexpr int dq_bc() {
+  return SPARSE ? 64 : dq_tile_keys<D, IS_BF16, CAUSAL>();
+}
+
+template <int D, int BQ_>
 struct Dkdv {
   static constexpr int NT = 256;       // 4 waves
   static constexpr int BKV = 128;      // keys per workgroup (32 per wave)
-  // Queries per step: 64, or 32 at d = 256, where dK and dV alone fill 256 accumulator
-  // registers and K and V another 128 (one wave per SIMD, the whole register file).
-  static constexpr int BQ = D >= 256 ? 32 : 64;
+  // Queries per step (from the table; 32 at d = 256, where dK and dV alone fill 256 accumulator
+  // registers and K and V another 128: one wave per SIMD, the whole register file).
+  static constexpr int BQ = BQ_;
   static constexpr int QBS = BQ / 32;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
@@ -250,14 +262,13 @@ struct Dkdv {
   static constexpr int STAGE = 2 * TILE + 2 * BQ * 2;  // Q, dO, then LSE*log2e and D (fp32)
   static constexpr int LDS_BYTES = 2 * STAGE * 2;
   static constexpr int LD_INSTR = BQ * D * 2 / 1024;  // 1 KB direct loads per tile and tensor
-  static constexpr int MIN_WG = (D <= 64) ? 2 : 1;
   // Dropout instances: one 32-bit keep word per (wave, query of the step) after the stages.
   static constexpr int MASK_BYTES = 4 * BQ * 4;
 };
 
 template <int D, bool IS_BF16, bool G_F32, bool CAUSAL, bool DROP, bool SPARSE>
-__global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs a) {
-  using C = Dkdv<D>;
+__global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void bwd_dkdv_kernel(BwdArgs a) {
+  using C = Dkdv<D, dkdv_bq<D, IS_BF16, CAUSAL, SPARSE>()>;
   static_assert(!(DROP && SPARSE), "the dropout words and the sparse list share one LDS area");
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
@@ -554,28 +565,27 @@ __global__ __launch_bounds__(256, Dkdv<D>::MIN_WG) void bwd_dkdv_kernel(BwdArgs 
 // ----------------------------------------------------------------------------------------
 // 3. dQ: queries outer.
 // ----------------------------------------------------------------------------------------
-template <int D>
+template <int D, int BC_>
 struct Dq {
   static constexpr int NT = 256;   // 4 waves x 32 queries
   static constexpr int NW = 4;
   static constexpr int BR = 128;   // queries per workgroup
-  // Keys per K/V tile: 64, or 32 at d = 256 (fewer score registers next to the 256-wide Q, dO
-  // and dQ fragments).
-  static constexpr int BC = D >= 256 ? 32 : 64;
+  // Keys per K/V tile (from the table; 32 at d = 256: fewer score registers next to the
+  // 256-wide Q, dO and dQ fragments).
+  static constexpr int BC = BC_;
   static constexpr int KB = BC / 32;  // 32-key MFMA blocks per tile
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int TILE = BC * D;     // swizzled rows, no padding
   static constexpr int STAGE = 2 * TILE;  // K then V
-  static constexpr int LDS_BYTES = 2 * STAGE * 2;
   static constexpr int LD_INSTR = BC * D * 2 / 1024;  // 1 KB direct loads per tile and tensor
-  // Waves per SIMD the register allocation must allow (d = 256: one, the whole file).
-  static constexpr int MIN_WG = (D <= 64) ? kDqWaves64 : D <= 128 ? 2 : 1;
+  static constexpr int LDS_BYTES = 2 * STAGE * 2;
 };
 
 template <int D, bool IS_BF16, bool G_F32, bool CAUSAL, bool DROP, bool SPARSE>
-__global__ __launch_bounds__(256, Dq<D>::MIN_WG) void bwd_dq_kernel(BwdArgs a) {
-  using C = Dq<D>;
+__global__ __launch_bounds__(256, (D <= 64 ? kDqWaves64 : D <= 128 ? 2 : 1)) void bwd_dq_kernel(
+    BwdArgs a) {
+  using C = Dq<D, dq_bc<D, IS_BF16, CAUSAL, SPARSE>()>;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
   const int tid = threadIdx.x;
@@ -826,16 +836,17 @@ static hipError_t launch_grads(BwdArgs a, hipStream_t s, hipEvent_t ev_before,
                                hipEvent_t ev_after) {
   hipError_t e;
   if (ev_before && (e = hipEventRecord(ev_before, s)) != hipSuccess) return e;
-  a.n_tiles = (a.Nk + Dkdv<D>::BKV - 1) / Dkdv<D>::BKV;
+  using KV = Dkdv<D, dkdv_bq<D, IS_BF16, CAUSAL, SPARSE>()>;
+  using QT = Dq<D, dq_bc<D, IS_BF16, CAUSAL, SPARSE>()>;
+  a.n_tiles = (a.Nk + KV::BKV - 1) / KV::BKV;
   e = launch_dyn(bwd_dkdv_kernel<D, IS_BF16, G_F32, CAUSAL, DROP, SPARSE>, a.n_tiles * a.bh,
-                 Dkdv<D>::LDS_BYTES + (DROP ? Dkdv<D>::MASK_BYTES : 0) +
-                     (SPARSE ? kSparseListBytes : 0),
+                 KV::LDS_BYTES + (DROP ? KV::MASK_BYTES : 0) + (SPARSE ? kSparseListBytes : 0),
                  a, s);
   if (e != hipSuccess) return e;
   if (ev_after && (e = hipEventRecord(ev_after, s)) != hipSuccess) return e;
-  a.n_tiles = (a.N + Dq<D>::BR - 1) / Dq<D>::BR;
+  a.n_tiles = (a.N + QT::BR - 1) / QT::BR;
   return launch_dyn(bwd_dq_kernel<D, IS_BF16, G_F32, CAUSAL, DROP, SPARSE>, a.n_tiles * a.bh,
-                    Dq<D>::LDS_BYTES + (SPARSE ? kSparseListBytes : 0), a, s);
+                    QT::LDS_BYTES + (SPARSE ? kSparseListBytes : 0), a, s);
 }
 
 template <int D, bool IS_BF16, bool G_F32, bool DROP, bool SPARSE>

@@ -174,6 +174,18 @@ __device__ __forceinline__ float buf_ldf(__amdgpu_buffer_rsrc_t r, uint32_t byte
 // for the loop's own prefetches.
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Workgroup barrier without a memory fence (a fenced __syncthreads would also wait for every
+// outstanding load, including prefetches meant to stay in flight). The empty asm statements keep
+// the compiler from moving LDS accesses across it, and the scheduling barriers keep every other
+// instruction on its side.
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // A run of NF MFMAs whose operands come from LDS, fragment f read by read(f) (returning the
 // 16 bytes) and consumed by use(f, frag) in that order, with the read of fragment f + PRE
 // issued before the MFMA of fragment f. The scheduling barrier after each step keeps that

@@ -20,8 +20,8 @@
 //     B operand (no LDS round trip); V stays in key order in LDS and its transposed operand is
 //     read with ds_read_b64_tr_b16;
 //   * exp2 with scale*log2(e) folded into one FMA per score;
-//   * K/V tiles hold fwd_tile_keys<D>() keys (a per-head-dim table written by the tuner; 64 for
-//     block-sparse masks);
+//   * K/V tiles hold fwd_tile_keys<D, IS_BF16, CAUSAL>() keys (a table per head dim, dtype and
+//     causality written by the tuner; 64 for block-sparse masks);
 //   * K and V tiles are double-buffered in LDS (one barrier per K/V tile) and filled by direct
 //     buffer->LDS loads, issued for the next tile before the current tile's math: no staging
 //     registers, no LDS write instructions. Tile rows are unpadded and swizzled (swz_off), which
@@ -86,9 +86,9 @@ struct Fwd16 {
   static_assert(LD_INSTR % NW == 0, "each wave issues whole 1 KB loads");
 };
 
-template <int D, bool SPARSE>
+template <int D, bool IS_BF16, bool CAUSAL, bool SPARSE>
 constexpr int fwd_bc() {
-  return SPARSE ? 64 : fwd_tile_keys<D>();
+  return SPARSE ? 64 : fwd_tile_keys<D, IS_BF16, CAUSAL>();
 }
 
 // Queries per wave (32 per MFMA column block). Two blocks halve the LDS reads per MFMA but, at
@@ -108,7 +108,7 @@ constexpr int fwd_min_waves() {
 
 template <int D, bool IS_BF16, bool O_F32, bool CAUSAL, int QB, bool DROP, bool SPARSE>
 __global__ __launch_bounds__(256, fwd_min_waves<D>()) void fwd16_kernel(FwdArgs a) {
-  using C = Fwd16<D, QB, fwd_bc<D, SPARSE>()>;
+  using C = Fwd16<D, QB, fwd_bc<D, IS_BF16, CAUSAL, SPARSE>()>;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
   const int tid = threadIdx.x;
@@ -403,12 +403,14 @@ __global__ __launch_bounds__(256, fwd_min_waves<D>()) void fwd16_kernel(FwdArgs 
 //   waits for it at the end of that phase; group 1 issues V_{t+1} in phase 2t+1 (stage of
 //   V_{t-1}, read up to phase 2t) and waits for it at the end of phase 2t+2.
 // ----------------------------------------------------------------------------------------
-template <int D>
+constexpr int kPpRows = 256;  // queries per workgroup of the two-group kernel (8 waves x 32)
+
+template <int D, int BC_>
 struct FwdPP {
   static constexpr int NW = 8;
   static constexpr int NT = NW * 64;
-  static constexpr int BR = NW * 32;
-  static constexpr int BC = fwd_tile_keys<D>();
+  static constexpr int BR = kPpRows;
+  static constexpr int BC = BC_;
   static constexpr int KB = BC / 32;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
@@ -419,20 +421,9 @@ struct FwdPP {
   static_assert(LD_INSTR % 4 == 0, "each wave of a group issues whole 1 KB loads");
 };
 
-// Workgroup barrier without a memory fence: no wait on this wave's outstanding direct loads.
-// The empty asm statements keep the compiler from moving LDS accesses across it, and the
-// scheduling barriers keep every other instruction on its side, so the phases stay phases.
-__device__ __forceinline__ void wg_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 template <int D, bool IS_BF16, bool O_F32, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void fwd16pp_kernel(FwdArgs a) {
-  using C = FwdPP<D>;
+  using C = FwdPP<D, fwd_tile_keys<D, IS_BF16, CAUSAL>()>;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
   const int tid = threadIdx.x;
@@ -817,7 +808,7 @@ __global__ __launch_bounds__(256, 2) void fwd32_kernel(FwdArgs a) {
 // ----------------------------------------------------------------------------------------
 template <int D, bool IS_BF16, bool O_F32, bool CAUSAL, int QB, bool DROP, bool SPARSE>
 static hipError_t launch16(FwdArgs a, hipStream_t s) {
-  using C = Fwd16<D, QB, fwd_bc<D, SPARSE>()>;
+  using C = Fwd16<D, QB, fwd_bc<D, IS_BF16, CAUSAL, SPARSE>()>;
   a.n_tiles = (a.N + C::BR - 1) / C::BR;
   const int grid = a.n_tiles * a.bh;
   constexpr int lds = C::LDS_BYTES + (SPARSE ? kSparseListBytes : 0);
@@ -831,7 +822,7 @@ static hipError_t launch16(FwdArgs a, hipStream_t s) {
 
 template <int D, bool IS_BF16, bool O_F32, bool CAUSAL>
 static hipError_t launch16pp(FwdArgs a, hipStream_t s) {
-  using C = FwdPP<D>;
+  using C = FwdPP<D, fwd_tile_keys<D, IS_BF16, CAUSAL>()>;
   a.n_tiles = (a.N + C::BR - 1) / C::BR;
   const int grid = a.n_tiles * a.bh;
   constexpr int lds = C::LDS_BYTES;
@@ -855,7 +846,7 @@ static hipError_t launch16_m(FwdArgs a, bool causal, hipStream_t s) {
     // twice as many, and a causal grid's longest workgroup is half as long. Measured on MI355X:
     // B=4 H=16 N=1024 d=64 causal 22 vs 25 us, non-causal 28 vs 26 us (two-group faster);
     // B=1 H=16 N=1024 d=128 27 vs 36 us.
-    const long long pp_blocks = (long long)((a.N + FwdPP<D>::BR - 1) / FwdPP<D>::BR) * a.bh;
+    const long long pp_blocks = (long long)((a.N + kPpRows - 1) / kPpRows) * a.bh;
     if (pp_blocks >= (causal ? kFwdPpMinBlocks : kFwdPpMinBlocks / 2))
       return causal ? launch16pp<D, IS_BF16, O_F32, true>(a, s)
                     : launch16pp<D, IS_BF16, O_F32, false>(a, s);

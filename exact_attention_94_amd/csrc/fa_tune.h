@@ -1,29 +1,24 @@
-// Tile configuration table of the 16-bit forward kernel: keys per K/V tile for each head
-// dimension ("FlashAttention 为什么不需要存下注意力矩阵" §05, first difference: production kernels
-// pick their block sizes per head dimension, dtype and causality among precompiled
-// configurations, by measurement rather than by formula).
+// Tile configuration table of the 16-bit kernels, per head dimension, input dtype and causality
+// ("FlashAttention 为什么不需要存下注意力矩阵" §05, first difference: production kernels pick their
+// block sizes per head dimension, dtype and causality among precompiled configurations, by
+// measurement rather than by formula):
+//   forward:          keys per K/V tile (32, 64 or 128);
+//   backward dK/dV:   queries per step of the keys-outer kernel (32 or 64);
+//   backward dQ:      keys per K/V tile of the queries-outer kernel (32 or 64).
+// A candidate is valid when its tile is a whole number of 1 KB direct loads per wave of four
+// (tile * d * 2 bytes a multiple of 4 KB); invalid entries fall back to 64.
 //
-// Written by exact_attention_94_amd/tune.py from timings on MI355X (gfx950) of the candidate
-// widths 32, 64 and 128 at B=2 H=16 N=4096 causal bf16 (per head dim); each value can be
-// overridden at build time with -DFA_FWD_BC_<d>=<keys>. The block-sparse instances always use
-// 64 keys (half a 128-key mask block).
+// The tables below are written by exact_attention_94_amd/tune.py from timings on MI355X (gfx950)
+// at B=2 H=16 N=4096 (exact_attention_94_amd/tuning/tiles_mi355x.json). Index order:
+// [head dim 32, 64, 96, 128][dtype f16, bf16][causal no, yes]. Candidate builds override every
+// entry at once with -DFA_FWD_BC_ALL=<keys>, -DFA_DKDV_BQ_ALL=<queries>, -DFA_DQ_BC_ALL=<keys>.
+// Block-sparse instances always use 64 (half a 128 x 128 mask block) and d = 256 its own fixed
+// tiles (32 keys forward, 32 queries dK/dV, 32 keys dQ).
 #pragma once
 
-#ifndef FA_FWD_BC_32
-#define FA_FWD_BC_32 128
-#endif
-#ifndef FA_FWD_BC_64
-#define FA_FWD_BC_64 128
-#endif
-#ifndef FA_FWD_BC_96
-#define FA_FWD_BC_96 64
-#endif
-#ifndef FA_FWD_BC_128
-#define FA_FWD_BC_128 64
-#endif
-#ifndef FA_FWD_BC_256
-#define FA_FWD_BC_256 32
-#endif
+#define FA_FWD_BC_TABLE {{{128, 128}, {128, 128}}, {{128, 128}, {128, 128}}, {{64, 64}, {64, 64}}, {{64, 64}, {64, 64}}}
+#define FA_DKDV_BQ_TABLE {{{64, 64}, {64, 64}}, {{64, 64}, {64, 64}}, {{64, 64}, {64, 64}}, {{64, 64}, {64, 64}}}
+#define FA_DQ_BC_TABLE {{{64, 64}, {64, 64}}, {{64, 64}, {32, 64}}, {{64, 64}, {64, 64}}, {{64, 32}, {64, 32}}}
 
 // LDS operand reads kept in flight ahead of the MFMAs of the score products (forward S, and S
 // with dP in both backward kernels); overridable with -DFA_FWD_PRE / -DFA_DKDV_PRE / -DFA_DQ_PRE.
@@ -66,13 +61,52 @@ constexpr int dq_pre() {
 constexpr int kDqWaves64 = FA_DQ_WAVES_64;
 constexpr int kFwdPpMinBlocks = FA_FWD_PP_MIN_BLOCKS;
 
+constexpr int kFwdBcTable[4][2][2] = FA_FWD_BC_TABLE;
+constexpr int kDkdvBqTable[4][2][2] = FA_DKDV_BQ_TABLE;
+constexpr int kDqBcTable[4][2][2] = FA_DQ_BC_TABLE;
+
+// Row of the tables for a head dimension (32, 64, 96, 128).
 template <int D>
+constexpr int tune_row() {
+  return D == 32 ? 0 : D == 64 ? 1 : D == 96 ? 2 : 3;
+}
+
+// Whole 1 KB direct loads for each of four waves: tile * D * 2 bytes a multiple of 4 KB.
+template <int D>
+constexpr bool whole_loads(int tile) {
+  return (tile * D * 2) % 4096 == 0;
+}
+
+template <int D>
+constexpr int valid_or_64(int tile) {
+  return whole_loads<D>(tile) ? tile : 64;
+}
+
+template <int D, bool IS_BF16, bool CAUSAL>
 constexpr int fwd_tile_keys() {
-  return D == 32    ? FA_FWD_BC_32
-         : D == 64  ? FA_FWD_BC_64
-         : D == 96  ? FA_FWD_BC_96
-         : D == 128 ? FA_FWD_BC_128
-                    : FA_FWD_BC_256;
+#ifdef FA_FWD_BC_ALL
+  if constexpr (D <= 128) return valid_or_64<D>(FA_FWD_BC_ALL);
+#endif
+  if constexpr (D > 128) return 32;
+  else return valid_or_64<D>(kFwdBcTable[tune_row<D>()][IS_BF16 ? 1 : 0][CAUSAL ? 1 : 0]);
+}
+
+template <int D, bool IS_BF16, bool CAUSAL>
+constexpr int dkdv_step_queries() {
+#ifdef FA_DKDV_BQ_ALL
+  if constexpr (D <= 128) return valid_or_64<D>(FA_DKDV_BQ_ALL);
+#endif
+  if constexpr (D > 128) return 32;
+  else return valid_or_64<D>(kDkdvBqTable[tune_row<D>()][IS_BF16 ? 1 : 0][CAUSAL ? 1 : 0]);
+}
+
+template <int D, bool IS_BF16, bool CAUSAL>
+constexpr int dq_tile_keys() {
+#ifdef FA_DQ_BC_ALL
+  if constexpr (D <= 128) return valid_or_64<D>(FA_DQ_BC_ALL);
+#endif
+  if constexpr (D > 128) return 32;
+  else return valid_or_64<D>(kDqBcTable[tune_row<D>()][IS_BF16 ? 1 : 0][CAUSAL ? 1 : 0]);
 }
 
 }  // namespace fa
