@@ -41,22 +41,31 @@ namespace fa {
 // ----------------------------------------------------------------------------------------
 // Workgroup -> (b*h, query tile) map. Workgroups are dispatched round-robin over the 8 XCDs
 // (blockIdx % 8). When B*H is a multiple of 8, each XCD gets a contiguous set of heads, and
-// within an XCD the longest query tiles (causal: the last ones) are dispatched first.
+// within an XCD the longest query tiles (causal: the last ones) are dispatched first. With
+// `fold` (a causal grid that is resident all at once, two workgroups per CU), the first half of
+// the order still runs longest-first and takes the first slot of each CU, while the second half
+// runs shortest-first: the second slot of the CU that got query tile T-1-t gets tile t, so every
+// CU holds about the same number of key tiles (tile t of a causal head visits t+1 of them).
 // ----------------------------------------------------------------------------------------
+__device__ __forceinline__ int causal_tile(int t, int n_tiles, bool fold) {
+  const int half = (n_tiles + 1) >> 1;
+  return (fold && t >= half) ? t - half : n_tiles - 1 - t;
+}
+
 __device__ __forceinline__ void map_block(int bid, int n_tiles, int bh_total, bool causal,
-                                          int& bh, int& tile) {
+                                          bool fold, int& bh, int& tile) {
+  int t;
   if ((bh_total & 7) == 0) {
     const int xcd = bid & 7;
     const int slot = bid >> 3;
     const int heads_per_xcd = bh_total >> 3;
-    const int t = slot / heads_per_xcd;
+    t = slot / heads_per_xcd;
     bh = xcd * heads_per_xcd + (slot - t * heads_per_xcd);
-    tile = causal ? (n_tiles - 1 - t) : t;
   } else {
-    const int t = bid / bh_total;
+    t = bid / bh_total;
     bh = bid - t * bh_total;
-    tile = causal ? (n_tiles - 1 - t) : t;
   }
+  tile = causal ? causal_tile(t, n_tiles, fold) : t;
 }
 
 // Key held by LDS row R (0..31 within a 32-key block) of a K tile: rows are filled so that
@@ -123,7 +132,7 @@ __global__ __launch_bounds__(256, fwd_min_waves<D>()) void fwd16_kernel(FwdArgs 
   const int qoff = a.qoff;
 
   int bh, tile;
-  map_block(blockIdx.x, a.n_tiles, a.bh, CAUSAL, bh, tile);
+  map_block(blockIdx.x, a.n_tiles, a.bh, CAUSAL, a.fold != 0, bh, tile);
   const size_t head_off = (size_t)bh * N * D;
   const size_t kv_off = (size_t)bh * Nk * D;
   const auto qrs = make_rsrc(static_cast<const uint16_t*>(a.q) + head_off, (uint32_t)N * D * 2);
@@ -438,7 +447,7 @@ __global__ __launch_bounds__(512, 1) void fwd16pp_kernel(FwdArgs a) {
   const int qoff = a.qoff;
 
   int bh, tile;
-  map_block(blockIdx.x, a.n_tiles, a.bh, CAUSAL, bh, tile);
+  map_block(blockIdx.x, a.n_tiles, a.bh, CAUSAL, a.fold != 0, bh, tile);
   const size_t head_off = (size_t)bh * N * D;
   const size_t kv_off = (size_t)bh * Nk * D;
   const auto qrs = make_rsrc(static_cast<const uint16_t*>(a.q) + head_off, (uint32_t)N * D * 2);
@@ -700,7 +709,7 @@ __global__ __launch_bounds__(256, 2) void fwd32_kernel(FwdArgs a) {
   const int N = a.N;
 
   int bh, tile;
-  map_block(blockIdx.x, a.n_tiles, a.bh, CAUSAL, bh, tile);
+  map_block(blockIdx.x, a.n_tiles, a.bh, CAUSAL, a.fold != 0, bh, tile);
   const size_t head_off = (size_t)bh * N * D;
   const float* __restrict__ qh = static_cast<const float*>(a.q) + head_off;
   const float* __restrict__ kh = static_cast<const float*>(a.k) + head_off;
@@ -806,11 +815,24 @@ __global__ __launch_bounds__(256, 2) void fwd32_kernel(FwdArgs a) {
 // ----------------------------------------------------------------------------------------
 // Host-side launchers (called by the C ABI after validation).
 // ----------------------------------------------------------------------------------------
+// Compute units of the current device (the runtime caches the attribute).
+static int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    return 256;
+  return n;
+}
+
 template <int D, bool IS_BF16, bool O_F32, bool CAUSAL, int QB, bool DROP, bool SPARSE>
 static hipError_t launch16(FwdArgs a, hipStream_t s) {
   using C = Fwd16<D, QB, fwd_bc<D, IS_BF16, CAUSAL, SPARSE>()>;
   a.n_tiles = (a.N + C::BR - 1) / C::BR;
   const int grid = a.n_tiles * a.bh;
+  // Two workgroups per CU (two waves per SIMD): a causal grid of more than one and at most two
+  // per CU is resident at once, so its long and short tiles are paired per CU.
+  a.fold = (CAUSAL && fwd_min_waves<D>() == 2 && grid > cu_count() && grid <= 2 * cu_count() &&
+            a.n_tiles > 1) ? 1 : 0;
   constexpr int lds = C::LDS_BYTES + (SPARSE ? kSparseListBytes : 0);
   auto kern = fwd16_kernel<D, IS_BF16, O_F32, CAUSAL, QB, DROP, SPARSE>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),

@@ -28,6 +28,10 @@ struct FwdArgs {
   int qoff;     // position of query row 0 in the key sequence (causal alignment), usually 0
   int bh;       // B * H
   int n_tiles;  // query tiles per head (set by the launcher)
+  // Causal grids resident in one round at two workgroups per CU (set by the launcher): the
+  // second half of the tile order runs shortest-first, so that each CU pairs a long query tile
+  // with a short one.
+  int fold;
   float c;      // scale * log2(e), never 0
   DropParams drop;  // used only by the dropout instances
   SparseParams sparse;  // used only by the block-sparse instances
