@@ -397,7 +397,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void bwd_dkdv_kernel(BwdArg
       // that P = 0 there.
       if (lane < C::BQ) {
         vec[lane] = (i0 + lane < N && lreg != -INFINITY) ? lreg * kLog2e : INFINITY;
-        vec[C::BQ + lane] = dreg;
+        vec[C::BQ + lane] = -dreg;
       }
     }
   };
@@ -412,14 +412,27 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void bwd_dkdv_kernel(BwdArg
     const float* del_s = lse_s + C::BQ;
 
     // S = Q K^T and dP = dO V^T (rows: queries in staged order, columns: this wave's keys).
-    f32x16 sacc[C::QBS], pacc[C::QBS];
+    // Without dropout the dP accumulators start at -D (slot i of block qb: the row vector entry
+    // of query 32qb + 16(i/8) + 8g + i%8), so that they end as dP - D; the first MFMA of each
+    // chain takes that block, or zero, as its accumulator input.
+    f32x16 sacc[C::QBS], pacc[C::QBS], pinit[C::QBS];
+    const f32x16 zero16 = {};
 #pragma unroll
-    for (int qb = 0; qb < C::QBS; ++qb)
+    for (int qb = 0; qb < C::QBS; ++qb) {
+      if constexpr (DROP) {
+        pinit[qb] = zero16;
+      } else {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sacc[qb][i] = 0.f;
-        pacc[qb][i] = 0.f;
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const f32x4 v =
+                *reinterpret_cast<const f32x4*>(del_s + qb * 32 + h * 16 + g * 8 + 4 * j);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pinit[qb][h * 8 + 4 * j + e] = v[e];
+          }
       }
+    }
     // Fragment f = (ks, qb, tensor: Q for S, dO for dP), read dkdv_pre<D>() ahead of its MFMA.
     read_ahead<2 * C::KS * C::QBS, dkdv_pre<D>()>(
         [&](int f) {
@@ -429,8 +442,8 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void bwd_dkdv_kernel(BwdArg
         },
         [&](int f, const Frag16& fr) {
           const int ks = f / (2 * C::QBS), qb = (f / 2) % C::QBS;
-          if (f & 1) pacc[qb] = mfma32x32x16<false>(fr, vf[ks], pacc[qb]);
-          else sacc[qb] = mfma32x32x16<false>(fr, kf[ks], sacc[qb]);
+          if (f & 1) pacc[qb] = mfma32x32x16<false>(fr, vf[ks], ks == 0 ? pinit[qb] : pacc[qb]);
+          else sacc[qb] = mfma32x32x16<false>(fr, kf[ks], ks == 0 ? zero16 : sacc[qb]);
         });
     // Mask (keys beyond Nk; causal: key after query + qoff) on the few tiles that need it, as a
     // score of -inf after scaling. Slot i holds query i0 + 32*qb + 16*(i/8) + 8*g + i%8.
@@ -470,8 +483,11 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void bwd_dkdv_kernel(BwdArg
         const int qloc = qb * 32 + h * 16 + g * 8;
         const f32x4 l0 = *reinterpret_cast<const f32x4*>(lse_s + qloc);
         const f32x4 l1 = *reinterpret_cast<const f32x4*>(lse_s + qloc + 4);
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(del_s + qloc);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(del_s + qloc + 4);
+        f32x4 d0 = {}, d1 = {};  // -D (dropout only: the dP accumulators then start at zero)
+        if constexpr (DROP) {
+          d0 = *reinterpret_cast<const f32x4*>(del_s + qloc);
+          d1 = *reinterpret_cast<const f32x4*>(del_s + qloc + 4);
+        }
         u32x4 mw0 = u32x4{0, 0, 0, 0}, mw1 = u32x4{0, 0, 0, 0};
         if constexpr (DROP) {
           mw0 = *reinterpret_cast<const u32x4*>(mask_w + qloc);
@@ -488,10 +504,11 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void bwd_dkdv_kernel(BwdArg
             const bool keep = (w >> r) & 1u;
             const float ks = a.drop.keep_scale;
             p[e] = keep ? pv * ks : 0.f;
-            ds[e] = pv * ((keep ? pacc[qb][h * 8 + e] * ks : 0.f) - dv);
+            ds[e] = pv * ((keep ? pacc[qb][h * 8 + e] * ks : 0.f) + dv);
           } else {
             p[e] = pv;
-            ds[e] = pv * (pacc[qb][h * 8 + e] - dv);
+            (void)dv;
+            ds[e] = pv * pacc[qb][h * 8 + e];
           }
         }
         pfr[qb][h].w = u32x4{pack2<false>(p[0], p[1]), pack2<false>(p[2], p[3]),
@@ -623,6 +640,9 @@ __global__ __launch_bounds__(256, (D <= 64 ? kDqWaves64 : D <= 128 ? 2 : 1)) voi
   // Per-query statistics, lane-local under the transposed layout. Rows beyond N: P = 0.
   const float lse_raw = buf_ldf(lrs, (uint32_t)qrow * 4);
   const float dlt = buf_ldf(drs, (uint32_t)qrow * 4);
+  f32x16 pinit;  // initial dP^T accumulator: -D without dropout, 0 with it
+#pragma unroll
+  for (int i = 0; i < 16; ++i) pinit[i] = DROP ? 0.f : -dlt;
 
   f32x16 dqacc[C::DB];
 #pragma unroll
@@ -688,15 +708,11 @@ __global__ __launch_bounds__(256, (D <= 64 ? kDqWaves64 : D <= 128 ? 2 : 1)) voi
     if (!live) return;
     const uint16_t* ks_ = smem + stage * C::STAGE;
     const uint16_t* vs_ = ks_ + C::TILE;
-    // S^T = K Q^T and dP^T = V dO^T: rows = keys (permuted), column = this lane's query.
+    // S^T = K Q^T and dP^T = V dO^T: rows = keys (permuted), column = this lane's query. Without
+    // dropout the dP^T chains start from the block -D of this lane's query (pinit), so that they
+    // end as dP^T - D.
     f32x16 sacc[C::KB], pacc[C::KB];
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sacc[kb][i] = 0.f;
-        pacc[kb][i] = 0.f;
-      }
+    const f32x16 zero16 = {};
     // Fragment f = (ks, kb, tensor: K for S^T, V for dP^T), read dq_pre<D>() ahead of its MFMA.
     read_ahead<2 * C::KS * C::KB, dq_pre<D>()>(
         [&](int f) {
@@ -706,8 +722,8 @@ __global__ __launch_bounds__(256, (D <= 64 ? kDqWaves64 : D <= 128 ? 2 : 1)) voi
         },
         [&](int f, const Frag16& fr) {
           const int ks = f / (2 * C::KB), kb = (f / 2) % C::KB;
-          if (f & 1) pacc[kb] = mfma32x32x16<false>(fr, of[ks], pacc[kb]);
-          else sacc[kb] = mfma32x32x16<false>(fr, qf[ks], sacc[kb]);
+          if (f & 1) pacc[kb] = mfma32x32x16<false>(fr, of[ks], ks == 0 ? pinit : pacc[kb]);
+          else sacc[kb] = mfma32x32x16<false>(fr, qf[ks], ks == 0 ? zero16 : sacc[kb]);
         });
     // Mask on the few tiles that need it. Slot i of block kb holds key
     // j0 + 32*kb + 16*(i/8) + 8*g + i%8.
@@ -740,7 +756,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? kDqWaves64 : D <= 128 ? 2 : 1)) voi
             const float dp = ((bits >> e) & 1u) ? pacc[kb][h * 8 + e] * a.drop.keep_scale : 0.f;
             ds[e] = pv * (dp - dlt);
           } else {
-            ds[e] = pv * (pacc[kb][h * 8 + e] - dlt);
+            ds[e] = pv * pacc[kb][h * 8 + e];
           }
         }
         dsf[kb][h].w = u32x4{pack2<false>(ds[0], ds[1]), pack2<false>(ds[2], ds[3]),

@@ -70,13 +70,19 @@ __device__ __forceinline__ float to_f32(uint16_t h) {
 // Value held by lane l ^ 32 (the other half of the wave), through the LDS crossbar.
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
 
+// IEEE 754-2019 maximum (NaN propagates, -inf is the identity). Chains of it become
+// v_maximum3_f32, without the canonicalising moves that fmaxf's NaN rule costs.
+__device__ __forceinline__ float vmax(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+
 // max / sum of x over lanes l and l ^ 32, with one v_permlane32_swap (VALU, no LDS). The swap
 // exchanges one half of the wave between its two operands; with both operands = x, the two
 // results hold x of lane l and of lane l ^ 32 in some order, so their max / sum is symmetric.
 __device__ __forceinline__ float halves_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
-  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float halves_min(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,

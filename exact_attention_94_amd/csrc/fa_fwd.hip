@@ -274,7 +274,7 @@ __global__ __launch_bounds__(256, fwd_min_waves<D>()) void fwd16_kernel(FwdArgs 
 #pragma unroll
           for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) red = __builtin_fmaxf(red, sacc[kb][qb][i]);
+            for (int i = 0; i < 16; ++i) red = vmax(red, sacc[kb][qb][i]);
           red = halves_max(red);
           const float m_blk = red * c;  // -inf when the whole tile is masked for this query
           // Exact running maximum: the largest weight of each row is then exp2(0) = 1, which
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(256, fwd_min_waves<D>()) void fwd16_kernel(FwdArgs 
           // saves the multiplies below but leaves that weight at 2^x with a rounding error of
           // up to 2^-9, which measurably degrades O, and through D = rowsum(dO * O) the
           // gradients, on peaked rows.)
-          const float m_new = __builtin_fmaxf(m_run[qb], m_blk);
+          const float m_new = vmax(m_run[qb], m_blk);
           const float corr = fast_exp2(m_run[qb] - m_new);
           m_run[qb] = m_new;
           l_run[qb] *= corr;
@@ -578,11 +578,9 @@ __global__ __launch_bounds__(512, 1) void fwd16pp_kernel(FwdArgs a) {
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) red4[i & 3] = __builtin_fmaxf(red4[i & 3], s[kb][i]);
-    float red = __builtin_fmaxf(__builtin_fmaxf(red4[0], red4[1]),
-                                __builtin_fmaxf(red4[2], red4[3]));
-    red = halves_max(red);
-    const float m_new = __builtin_fmaxf(m_run, red * c);
+      for (int i = (kb == 0 ? 4 : 0); i < 16; ++i) red4[i & 3] = vmax(red4[i & 3], s[kb][i]);
+    const float red = halves_max(vmax(vmax(red4[0], red4[1]), vmax(red4[2], red4[3])));
+    const float m_new = vmax(m_run, red * c);
     const float corr = fast_exp2(m_run - m_new);
     m_run = m_new;
     l_run *= corr;

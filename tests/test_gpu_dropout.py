@@ -80,7 +80,12 @@ def test_dropout_sweep(fa, dtype, d, causal):
             check("dV", host64(dv), g["dv"], 2e-2)
 
 
-def test_dropout_p0_is_bitwise_the_plain_path(fa):
+def test_dropout_p0_matches_the_plain_path(fa):
+    """With p = 0 the dropout kernels keep every score. The forward is bitwise the plain path.
+    The gradients agree to fp32 rounding of dP - D only: the plain kernels start the dP
+    accumulators at -D, while the dropout kernels scale dP first and subtract D afterwards. An
+    ulp of difference there can flip the fp16 rounding of a dS element, hence a bound far below
+    the oracle tolerance (2e-2) rather than equality."""
     import torch
     t = inp.draw((2, 2, 333, 64), "bf16", 8, with_do=True)
     q, k, v, do = (to_device(t[n]) for n in ("q", "k", "v", "do"))
@@ -91,8 +96,10 @@ def test_dropout_p0_is_bitwise_the_plain_path(fa):
                      seed=5)
     torch.cuda.synchronize()
     assert torch.equal(o0, o1) and torch.equal(l0, l1)
-    for x, y in zip(g0, g1):
-        assert torch.equal(x, y)
+    for name, x, y in zip(("dQ", "dK", "dV"), g0, g1):
+        diff = float((x - y).abs().max())
+        print(f"  {name}: max |plain - dropout p=0| = {diff:.3e}", flush=True)
+        assert diff <= 1e-4, (name, diff)
 
 
 def test_dropout_seed_and_offset_select_the_mask(fa):
