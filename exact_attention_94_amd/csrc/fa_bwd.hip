@@ -545,14 +545,19 @@ __global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void bwd_dkdv_kernel(BwdArg
   wait_vmem_all();
   store_vec(0, step_i0(0));
   __syncthreads();
+  // Nothing is loaded or waited for after the last step.
   for (int step = 0; step < n_live; step += 2) {
-    issue_tile(1, step_i0(step + 1));
+    const bool more1 = step + 1 < n_live;
+    if (more1) issue_tile(1, step_i0(step + 1));
     step_math(0, step_i0(step));
+    if (!more1) break;
     wait_vmem_all();
     store_vec(1, step_i0(step + 1));
     __syncthreads();
-    issue_tile(0, step_i0(step + 2));
+    const bool more2 = step + 2 < n_live;
+    if (more2) issue_tile(0, step_i0(step + 2));
     step_math(1, step_i0(step + 1));
+    if (!more2) break;
     wait_vmem_all();
     store_vec(0, step_i0(step + 2));
     __syncthreads();
@@ -780,13 +785,18 @@ __global__ __launch_bounds__(256, (D <= 64 ? kDqWaves64 : D <= 128 ? 2 : 1)) voi
     }
   };
 
+  // Nothing is loaded or waited for after the last tile.
   for (int jt = 0; jt < n_live; jt += 2) {
-    issue_tile(1, tile_j0(jt + 1));
+    const bool more1 = jt + 1 < n_live;
+    if (more1) issue_tile(1, tile_j0(jt + 1));
     tile_math(0, tile_j0(jt));
+    if (!more1) break;
     wait_vmem_all();
     __syncthreads();
-    issue_tile(0, tile_j0(jt + 2));
+    const bool more2 = jt + 2 < n_live;
+    if (more2) issue_tile(0, tile_j0(jt + 2));
     tile_math(1, tile_j0(jt + 1));
+    if (!more2) break;
     wait_vmem_all();
     __syncthreads();
   }

@@ -343,22 +343,26 @@ __global__ __launch_bounds__(256, fwd_min_waves<D>()) void fwd16_kernel(FwdArgs 
   };
 
   // n_kt >= 1 always (N >= 1). The prologue stages tile 0; the explicit wait retires the Q loads
-  // before the loop; tile 1 is then in flight when the loop starts. Every load and LDS write in
-  // the loop is unconditional (tiles past the end read zeros and their math is skipped), so the
-  // compiler counts outstanding loads exactly.
+  // before the loop; tile 1 is then in flight when the loop starts.
   issue_tile(0, tile_j0(0));
   wait_vmem_all();
   __syncthreads();
 
   // Iteration jt: start the direct loads of tile jt+1 into the other stage (its previous tile's
   // math ended before the last barrier), do the math of tile jt, wait for the loads, barrier.
+  // After the last tile nothing is loaded or waited for: on small grids the memory latency of a
+  // load whose data is never used would sit on the critical path of every workgroup.
   for (int jt = 0; jt < n_live; jt += 2) {
-    issue_tile(1, tile_j0(jt + 1));
+    const bool more1 = jt + 1 < n_live;
+    if (more1) issue_tile(1, tile_j0(jt + 1));
     tile_math(0, tile_j0(jt));
+    if (!more1) break;
     wait_vmem_all();
     __syncthreads();
-    issue_tile(0, tile_j0(jt + 2));
+    const bool more2 = jt + 2 < n_live;
+    if (more2) issue_tile(0, tile_j0(jt + 2));
     tile_math(1, tile_j0(jt + 1));
+    if (!more2) break;
     wait_vmem_all();
     __syncthreads();
   }
@@ -612,14 +616,14 @@ __global__ __launch_bounds__(512, 1) void fwd16pp_kernel(FwdArgs a) {
     m_phase(-1, 1, 0);
     wg_barrier();
     for (int t = 0; t < n_kt; t += 2) {
-      load_k(1, t + 1);
+      if (t + 1 < n_kt) load_k(1, t + 1);
       v_phase(t);
       wait_vmem_all();
       wg_barrier();
       m_phase(t, 0, 1);
       wg_barrier();
       if (t + 1 >= n_kt) break;
-      load_k(0, t + 2);
+      if (t + 2 < n_kt) load_k(0, t + 2);
       v_phase(t + 1);
       wait_vmem_all();
       wg_barrier();
@@ -632,14 +636,14 @@ __global__ __launch_bounds__(512, 1) void fwd16pp_kernel(FwdArgs a) {
       m_phase(t - 1, 1, 0);
       wait_vmem_all();
       wg_barrier();
-      load_v(1, t + 1);
+      if (t + 1 < n_kt) load_v(1, t + 1);
       v_phase(t);
       wg_barrier();
       if (t + 1 >= n_kt) break;
       m_phase(t, 0, 1);
       wait_vmem_all();
       wg_barrier();
-      load_v(0, t + 2);
+      if (t + 2 < n_kt) load_v(0, t + 2);
       v_phase(t + 1);
       wg_barrier();
     }
