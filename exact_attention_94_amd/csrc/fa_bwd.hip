@@ -74,7 +74,7 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t x, uint32_t* red) {
 }
 
 // 1a. Max pass. Workgroup bh * n_parts + p covers elements [p * chunk, (p + 1) * chunk) of head
-// bh (chunk a multiple of 2048) and writes the largest |dO| there, as the 16-bit magnitude
+// bh (chunk a multiple of 8192) and writes the largest |dO| there, as the 16-bit magnitude
 // pattern (for bf16 and fp16 alike, larger magnitudes have larger patterns), to dmax[bh][p].
 // For bf16 inputs it also writes the fp16 copy of the same elements of Q.
 template <int D, bool IS_BF16>
@@ -88,12 +88,30 @@ __global__ __launch_bounds__(256) void bwd_absmax_kernel(BwdArgs a, int chunk, i
   const int end = min(n, beg + chunk);
   const uint16_t* dout = static_cast<const uint16_t*>(a.dout) + head;
   uint32_t mx = 0;
-  for (int e = beg + (int)threadIdx.x * 8; e < end; e += 2048) {
-    const u32x4 w = ld16(dout + e);
+  // Four 2048-element strides per batch, all loads issued before any use, so that a batch waits
+  // for memory once rather than once per stride. The loads are unconditional through buffer
+  // resources over the head (zeros past its end); elements past this part's end but inside the
+  // head belong to another part of the same head, so counting them leaves the head's maximum
+  // unchanged.
+  const auto drs = make_rsrc(dout, (uint32_t)n * 2);
+  const auto qrs = make_rsrc(static_cast<const uint16_t*>(a.q) + head, (uint32_t)n * 2);
+  constexpr int U = 4;
+  for (int e0 = beg + (int)threadIdx.x * 8; e0 < end; e0 += U * 2048) {
+    u32x4 w[U], qv[U];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) mx = max(mx, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
-    if constexpr (IS_BF16)
-      st16(a.ws_q + head + e, to_f16x8<true>(ld16(static_cast<const uint16_t*>(a.q) + head + e)));
+    for (int u = 0; u < U; ++u) {
+      const uint32_t off = (uint32_t)(e0 + u * 2048) * 2;
+      w[u] = buf_ld16(drs, off);
+      if constexpr (IS_BF16) qv[u] = buf_ld16(qrs, off);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        mx = max(mx, max(w[u][i] & 0x7FFFu, (w[u][i] >> 16) & 0x7FFFu));
+      if constexpr (IS_BF16)
+        if (e0 + u * 2048 < end) st16(a.ws_q + head + e0 + u * 2048, to_f16x8<true>(qv[u]));
+    }
   }
   mx = block_max_u32(mx, red);
   if (threadIdx.x == 0) a.dmax[(size_t)bh * kMaxParts + p] = mx;
@@ -109,58 +127,84 @@ __device__ __forceinline__ int do_scale_exp(float amax) {
   return min(120, max(-120, 4 - ex));
 }
 
-// 1b. Preprocess, workgroup bh * n_rb + rb (row block rb of head bh): the head's dO scale 2^s
-// from the partial maxima, then for each row of the block D = 2^s rowsum(dO * O) in fp32 and the
-// fp16 copy of dO * 2^s (exact scaling, one rounding). Row block 0 stores 2^-s for the gradient
-// epilogues.
+// Partial maxima per head written by the max pass (at most 64, so that one wave reduces them) and
+// row blocks per workgroup of the preprocess: fewer, longer workgroups keep both passes near
+// memory bandwidth instead of paying a reduction per few kilobytes.
+constexpr int kPreParts = 64;
+constexpr int kPreBlocks = 4;
+static_assert(kPreParts <= kMaxParts, "partial maxima fit the workspace");
+
+// 1b. Preprocess, workgroup bh * n_rb + rb (row blocks kPreBlocks * rb .. of head bh): the
+// head's dO scale 2^s from the partial maxima, then for each row D = 2^s rowsum(dO * O) in fp32
+// and the fp16 copy of dO * 2^s (exact scaling, one rounding). Workgroup 0 of each head stores
+// 2^-s for the gradient epilogues.
 template <int D, bool IS_BF16, bool O_F32>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, int n_parts, int n_rb) {
   constexpr int TPR = pre_tpr<D>();
   constexpr int RPB = 256 / TPR;
-  __shared__ uint32_t red[4];
   const int t = threadIdx.x;
   const int bh = blockIdx.x / n_rb;
   const int rb = blockIdx.x - bh * n_rb;
-  const uint32_t part = t < n_parts ? a.dmax[(size_t)bh * kMaxParts + t] : 0u;
-  const float amax = to_f32<IS_BF16>((uint16_t)block_max_u32(part, red));
+  uint32_t part = (t & 63) < n_parts ? a.dmax[(size_t)bh * kMaxParts + (t & 63)] : 0u;
+  // All loads of the workgroup's row blocks first, then the math and the stores. The loads are
+  // unconditional through buffer resources over the head: rows past N, and the idle lanes of
+  // d = 96 (given an offset past the end), read zeros.
+  const int cc = t % TPR;
+  const size_t head = (size_t)bh * a.N * D;
+  const uint32_t n_el = (uint32_t)a.N * D;
+  const auto drs = make_rsrc(static_cast<const uint16_t*>(a.dout) + head, n_el * 2);
+  const auto ors = O_F32 ? make_rsrc(static_cast<const float*>(a.o) + head, n_el * 4)
+                         : make_rsrc(static_cast<const uint16_t*>(a.o) + head, n_el * 2);
+  u32x4 dw[kPreBlocks];
+  f32x4 of[kPreBlocks][2];
+#pragma unroll
+  for (int sub = 0; sub < kPreBlocks; ++sub) {
+    const int row = (rb * kPreBlocks + sub) * RPB + t / TPR;
+    const uint32_t el = cc < D / 8 ? (uint32_t)row * D + cc * 8 : n_el;
+    dw[sub] = buf_ld16(drs, el * 2);
+    if constexpr (O_F32) {
+      of[sub][0] = __builtin_bit_cast(f32x4, buf_ld16(ors, el * 4));
+      of[sub][1] = __builtin_bit_cast(f32x4, buf_ld16(ors, el * 4 + 16));
+    } else {
+      const u32x4 ow = buf_ld16(ors, el * 2);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        of[sub][w >> 1][2 * (w & 1)] = to_f32<IS_BF16>((uint16_t)(ow[w] & 0xFFFFu));
+        of[sub][w >> 1][2 * (w & 1) + 1] = to_f32<IS_BF16>((uint16_t)(ow[w] >> 16));
+      }
+    }
+  }
+  // The head's largest |dO| from its n_parts <= 64 partial maxima (loaded above), reduced by each
+  // wave on its own (no LDS, no barrier), and the dO scale 2^s it gives.
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) part = max(part, (uint32_t)__shfl_xor((int)part, off));
+  const float amax = to_f32<IS_BF16>((uint16_t)part);
   const int sexp = do_scale_exp(amax);
   const float up = ldexpf(1.f, sexp);
   if (rb == 0 && t == 0) a.gscale[bh] = ldexpf(1.f, -sexp);
-
-  const int row = rb * RPB + t / TPR;
-  const int cc = t % TPR;
-  const size_t base = ((size_t)bh * a.N + row) * D + cc * 8;
-  float acc = 0.f;
-  if (row < a.N && cc < D / 8) {
-    const u32x4 dw = ld16(static_cast<const uint16_t*>(a.dout) + base);
+#pragma unroll
+  for (int sub = 0; sub < kPreBlocks; ++sub) {
+    const int row = (rb * kPreBlocks + sub) * RPB + t / TPR;
+    const size_t base = head + (size_t)row * D + cc * 8;
     float dof[8];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      dof[2 * w] = to_f32<IS_BF16>((uint16_t)(dw[w] & 0xFFFFu));
-      dof[2 * w + 1] = to_f32<IS_BF16>((uint16_t)(dw[w] >> 16));
+      dof[2 * w] = to_f32<IS_BF16>((uint16_t)(dw[sub][w] & 0xFFFFu));
+      dof[2 * w + 1] = to_f32<IS_BF16>((uint16_t)(dw[sub][w] >> 16));
     }
-    if constexpr (O_F32) {
-      const float* op = static_cast<const float*>(a.o) + base;
-      const f32x4 o0 = *reinterpret_cast<const f32x4*>(op);
-      const f32x4 o1 = *reinterpret_cast<const f32x4*>(op + 4);
+    float acc = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc += dof[e] * o0[e] + dof[4 + e] * o1[e];
-    } else {
-      const u32x4 ow = ld16(static_cast<const uint16_t*>(a.o) + base);
+    for (int e = 0; e < 4; ++e) acc += dof[e] * of[sub][0][e] + dof[4 + e] * of[sub][1][e];
+    if (row < a.N && cc < D / 8) {
+      u32x4 o16;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        acc += dof[2 * w] * to_f32<IS_BF16>((uint16_t)(ow[w] & 0xFFFFu));
-        acc += dof[2 * w + 1] * to_f32<IS_BF16>((uint16_t)(ow[w] >> 16));
-      }
+      for (int w = 0; w < 4; ++w) o16[w] = pack2<false>(dof[2 * w] * up, dof[2 * w + 1] * up);
+      st16(a.ws_do + base, o16);
     }
-    u32x4 o16;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) o16[w] = pack2<false>(dof[2 * w] * up, dof[2 * w + 1] * up);
-    st16(a.ws_do + base, o16);
+    for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (row < a.N && cc == 0) a.delta[(size_t)bh * a.N + row] = acc * up;
   }
-#pragma unroll
-  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < a.N && cc == 0) a.delta[(size_t)bh * a.N + row] = acc * up;
 }
 
 // Debug range check (see fa_kernels.h).
@@ -820,11 +864,11 @@ __global__ __launch_bounds__(256, (D <= 64 ? kDqWaves64 : D <= 128 ? 2 : 1)) voi
 // ----------------------------------------------------------------------------------------
 // Launchers.
 // ----------------------------------------------------------------------------------------
-// Elements per workgroup of the max pass: the head split into at most kMaxParts slices of a
-// multiple of 2048 elements (256 threads x 8).
+// Elements per workgroup of the max pass: the head split into at most kPreParts slices of a
+// multiple of 8192 elements (256 threads x 8 elements x the pass's batch of 4 strides).
 inline int absmax_chunk(long long head_elems) {
-  const long long per = (head_elems + kMaxParts - 1) / kMaxParts;
-  return (int)((per + 2047) / 2048 * 2048);
+  const long long per = (head_elems + kPreParts - 1) / kPreParts;
+  return (int)((per + 8191) / 8192 * 8192);
 }
 
 template <int D, bool IS_BF16>
@@ -837,7 +881,7 @@ static hipError_t launch_pre(const BwdArgs& a, bool o_f32, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int RPB = 256 / pre_tpr<D>();
-  const int n_rb = (a.N + RPB - 1) / RPB;
+  const int n_rb = (a.N + RPB * kPreBlocks - 1) / (RPB * kPreBlocks);
   const dim3 grid(n_rb * a.bh);
   if (o_f32)
     hipLaunchKernelGGL((bwd_pre_kernel<D, IS_BF16, true>), grid, dim3(256), 0, s, a, n_parts,
