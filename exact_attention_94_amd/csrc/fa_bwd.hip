@@ -311,7 +311,7 @@ struct Dkdv {
 };
 
 template <int D, bool IS_BF16, bool G_F32, bool CAUSAL, bool DROP, bool SPARSE>
-__global__ __launch_bounds__(256, (D <= 64 ? 2 : 1)) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, (D <= 64 ? kDkdvWaves64 : 1)) void bwd_dkdv_kernel(BwdArgs a) {
   using C = Dkdv<D, dkdv_bq<D, IS_BF16, CAUSAL, SPARSE>()>;
   static_assert(!(DROP && SPARSE), "the dropout words and the sparse list share one LDS area");
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];

@@ -37,6 +37,10 @@
 #ifndef FA_FWD_PP_MIN_BLOCKS
 #define FA_FWD_PP_MIN_BLOCKS 512
 #endif
+// Waves per SIMD the dK/dV kernel's register allocation must allow at d <= 64.
+#ifndef FA_DKDV_WAVES_64
+#define FA_DKDV_WAVES_64 2
+#endif
 // Waves per SIMD the dQ kernel's register allocation must allow at d <= 64.
 #ifndef FA_DQ_WAVES_64
 #define FA_DQ_WAVES_64 2
@@ -59,6 +63,7 @@ constexpr int dq_pre() {
   return D == 64 ? FA_DQ_PRE : 0;
 }
 constexpr int kDqWaves64 = FA_DQ_WAVES_64;
+constexpr int kDkdvWaves64 = FA_DKDV_WAVES_64;
 constexpr int kFwdPpMinBlocks = FA_FWD_PP_MIN_BLOCKS;
 
 constexpr int kFwdBcTable[4][2][2] = FA_FWD_BC_TABLE;
