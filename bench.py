@@ -20,6 +20,8 @@ of them is part of the headline value.
 
 Before timing, W warm-up steps run and then untimed steps continue for --settle-ms (default
 500 ms): the first tens of milliseconds of load from idle run ~15% slower than the steady state.
+Each of the secondary timings below first repeats its own calls untimed for about 150 ms, for the
+same reason (a small workload right after a different one otherwise reads up to ~50% slow).
 
 Next to the mean step time the line gives the median and minimum of the per-step times of the
 breakdown loop, the mean step time with the caches flushed before each step (cold_step_ms), and
@@ -231,6 +233,20 @@ def cpu_baseline(w, t, heads=2, repeats=3):
             "configs": configs}
 
 
+def settle(fn, ms=150.0, batch=10, cap=3000):
+    """Untimed calls of fn for about `ms` milliseconds before a timed loop: the first tens of
+    milliseconds of a new load run slower (clocks and power ramp up), as before the headline."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < ms and n < cap:
+        for _ in range(batch):
+            fn()
+        torch.cuda.synchronize()
+        n += batch
+    return n
+
+
 def time_dropout(fa, ev, stream, w, q, k, v, do, o, lse, grads, ws, steps, p=0.1):
     """The same step with dropout (keep mask regenerated from seed and offset in every kernel):
     forward and backward times, reported beside the headline (which has no dropout)."""
@@ -249,6 +265,7 @@ def time_dropout(fa, ev, stream, w, q, k, v, do, o, lse, grads, ws, steps, p=0.1
         fwd(i)
         bwd(i)
     torch.cuda.synchronize()
+    settle(lambda: (fwd(0), bwd(0)))
     e = [[ev.create() for _ in range(3)] for _ in range(steps)]
     for i in range(steps):
         ev.record(e[i][0], stream)
@@ -303,6 +320,7 @@ def time_blocksparse(fa, ev, stream, w, q, k, v, do, o, lse, grads, ws, steps):
         fwd()
         bwd()
     torch.cuda.synchronize()
+    settle(lambda: (fwd(), bwd()))
     e = [[ev.create() for _ in range(3)] for _ in range(steps)]
     for i in range(steps):
         ev.record(e[i][0], stream)
@@ -363,8 +381,9 @@ def gpu_clock_mhz():
 
 
 def time_workloads(fa, ev, stream, dev, steps):
-    """The other named workloads, timed the same way (one event pair around `steps` back-to-back
-    calls): B=4 H=16 N=1024 d=64 forward, causal and not (O in bf16); B=1 H=32 N=8192 d=128 with
+    """The other named workloads, timed the same way (a settle phase, then one event pair around
+    `steps` back-to-back calls): B=4 H=16 N=1024 d=64 forward, causal and not (O in bf16);
+    B=1 H=32 N=8192 d=128 with
     Q and K scaled by 2 (peaked rows), forward (fp32 O) and backward (fp32 gradients), causal;
     B=1 H=8 N=32768 d=128 causal forward (O in bf16). Inputs are normal draws of the workloads'
     shapes; FLOPs follow the headline convention."""
@@ -375,6 +394,7 @@ def time_workloads(fa, ev, stream, dev, steps):
         for _ in range(2):
             fn()
         torch.cuda.synchronize()
+        settle(fn)
         e0, e1 = ev.create(), ev.create()
         ev.record(e0, stream)
         for _ in range(n):
@@ -454,6 +474,7 @@ def time_decode(fa, ev, stream, dev, steps, B=4, H=32, nk=16384, d=128):
     for _ in range(3):
         fa.decode(q, k, v, causal=True, out=out, lse=lse, workspace=ws)
     torch.cuda.synchronize()
+    settle(lambda: fa.decode(q, k, v, causal=True, out=out, lse=lse, workspace=ws))
     e0, e1 = ev.create(), ev.create()
     ev.record(e0, stream)
     for _ in range(steps):
