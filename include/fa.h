@@ -19,8 +19,8 @@
  * vectors are contiguous [B, H, N]. Q, K and V share N (self-attention). Pointers must be
  * device pointers (hipMalloc'd or equivalent) aligned to 16 bytes.
  *
- * Supported: d in {32, 64, 96, 128}, and 256 for the plain 16-bit forward (fa_forward,
- * fa_forward_kv) only; decoding: d in {64, 128}. N >= 1 (a ragged tail is masked);
+ * Supported: d in {32, 64, 96, 128}, and 256 for plain 16-bit attention only (fa_forward,
+ * fa_forward_kv, fa_backward, fa_backward_kv); decoding: d in {64, 128}. N >= 1 (a ragged tail is masked);
  * B, H >= 1 with B*H*N*d < 2^31
  * and N*d <= 2^30;
  * in_dtype in {FA_F32, FA_F16, FA_BF16}; any finite scale; causal in {0, 1}.
@@ -91,9 +91,10 @@ fa_status fa_forward_kv(const void* q, const void* k, const void* v, void* o, fl
 
 /*
  * Bytes of device workspace fa_backward needs for these sizes and dtypes: the row vector
- * D = rowsum(dO * O) (float32 [B,H,N]), a per-head dO scale (float32 [B,H]), 256 partial maxima
- * of |dO| per head, a flag word, the scaled fp16 copy of dO ([B,H,N,d] 16-bit) and, when in_dtype
- * is FA_BF16, fp16 copies of Q, K and V (3 x [B,H,N,d] 16-bit) used as the MFMA operands.
+ * D = rowsum(dO * O) (float32 [B,H,N]), a per-head dO scale (float32 [B,H]), room for 256
+ * partial maxima of |dO| per head, a flag word, the scaled fp16 copy of dO ([B,H,N,d] 16-bit)
+ * and, when in_dtype is FA_BF16, fp16 copies of Q, K and V (3 x [B,H,N,d] 16-bit) used as the
+ * MFMA operands.
  * grad_dtype does not change the size but is validated. Returns 0 for arguments fa_backward would
  * reject (e.g. an in_dtype / grad_dtype pair it does not provide).
  */
