@@ -76,6 +76,12 @@ __device__ __forceinline__ float vmax(float a, float b) {
   return __builtin_elementwise_maximum(a, b);
 }
 
+// acc + lo + hi of the two fp16 values packed in w, in fp32: one v_dot2c_f32_f16 against (1, 1).
+__device__ __forceinline__ float add_pair_f16(uint32_t w, float acc) {
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
+}
+
 // max / sum of x over lanes l and l ^ 32, with one v_permlane32_swap (VALU, no LDS). The swap
 // exchanges one half of the wave between its two operands; with both operands = x, the two
 // results hold x of lane l and of lane l ^ 32 in some order, so their max / sum is symmetric.

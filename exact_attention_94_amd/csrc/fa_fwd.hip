@@ -589,7 +589,13 @@ __global__ __launch_bounds__(512, 1) void fwd16pp_kernel(FwdArgs a) {
     m_run = m_new;
     l_run *= corr;
     corr_pend = corr;
+    // Row sum. bf16: the unrounded fp32 probabilities (a bf16 rounding of a dominant weight would
+    // show in log l beyond the LSE tolerance). fp16: the probabilities as rounded for the P.V
+    // product, two per v_dot2c_f32_f16 in four chains; an fp16 rounding (2^-11 relative) stays
+    // well inside that tolerance, and O is then normalised by the sum of exactly the weights
+    // that multiplied V.
     float lsum = 0.f;
+    float lpart[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
@@ -598,11 +604,16 @@ __global__ __launch_bounds__(512, 1) void fwd16pp_kernel(FwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           p[e] = fast_exp2(__builtin_fmaf(s[kb][h * 8 + e], c, -m_new));
-          lsum += p[e];
+          if constexpr (IS_BF16) lsum += p[e];
         }
         pf[kb][h].w = u32x4{pack2<IS_BF16>(p[0], p[1]), pack2<IS_BF16>(p[2], p[3]),
                             pack2<IS_BF16>(p[4], p[5]), pack2<IS_BF16>(p[6], p[7])};
+        if constexpr (!IS_BF16) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) lpart[j] = add_pair_f16(pf[kb][h].w[j], lpart[j]);
+        }
       }
+    if constexpr (!IS_BF16) lsum = (lpart[0] + lpart[1]) + (lpart[2] + lpart[3]);
     l_run += lsum;
   };
 
