@@ -25,7 +25,7 @@ fa_status check_shape(int B, int H, int N, int d) {
   if (elems > 0x7FFFFFFFLL) return FA_ERR_INVALID_ARG;
   // Per-head byte offsets (and the prefetches a few tiles past N) must fit the 32-bit offsets
   // of buffer loads.
-  if ((long long)N * d > (1LL << 30)) return FA_ERR_INVALID_ARG;
+  if ((long long)N * d >= (1LL << 30)) return FA_ERR_INVALID_ARG;
   if (d != 32 && d != 64 && d != 96 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
@@ -402,7 +402,7 @@ struct DecLayout {
 fa_status decode_layout(int B, int H, int Nq, int Nk, int d, DecLayout& L) {
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_ERR_INVALID_ARG;
   if ((long long)B * H * Nk * d > 0x7FFFFFFFLL) return FA_ERR_INVALID_ARG;
-  if ((long long)Nk * d > (1LL << 30)) return FA_ERR_INVALID_ARG;
+  if ((long long)Nk * d >= (1LL << 30)) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (Nq > 4) return FA_ERR_UNSUPPORTED;
   if (Nq > Nk) return FA_ERR_INVALID_ARG;

@@ -22,7 +22,8 @@
  * Supported: d in {32, 64, 96, 128}, and 256 for plain 16-bit attention only (fa_forward,
  * fa_forward_kv, fa_backward, fa_backward_kv); decoding: d in {64, 128}. N >= 1 (a ragged tail is masked);
  * B, H >= 1 with B*H*N*d < 2^31
- * and N*d <= 2^30;
+ * and N*d < 2^30 (a head's fp32 rows then span less than 4 GiB, the reach of a buffer load's
+ * 32-bit byte range; the same bound applies to Nk*d);
  * in_dtype in {FA_F32, FA_F16, FA_BF16}; any finite scale; causal in {0, 1}.
  * The backward supports all three input dtypes (fp32 inputs: O and the gradients in fp32, N = Nk,
  * no dropout or block mask, as the fp32 forward).

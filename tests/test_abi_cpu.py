@@ -91,6 +91,9 @@ def bwd(**kw):
     (dict(B=-1), B.FA_ERR_INVALID_ARG),
     (dict(B=1 << 16, H=1 << 10, N=1 << 10), B.FA_ERR_INVALID_ARG),
     (dict(B=1, H=1, N=(1 << 24) + 1), B.FA_ERR_INVALID_ARG),
+    # N*d = 2^30: a head of fp32 O would span exactly 4 GiB, past a 32-bit buffer range.
+    (dict(B=1, H=1, N=1 << 24), B.FA_ERR_INVALID_ARG),
+    (dict(B=1, H=1, N=(1 << 23), d=128), B.FA_ERR_INVALID_ARG),
     (dict(scale=float("nan")), B.FA_ERR_INVALID_ARG),
     (dict(scale=float("inf")), B.FA_ERR_INVALID_ARG),
     (dict(causal=2), B.FA_ERR_INVALID_ARG),
@@ -110,6 +113,7 @@ def test_forward_rejects(kw, status):
     (dict(dq=None), B.FA_ERR_INVALID_ARG),
     (dict(do=P + 4), B.FA_ERR_INVALID_ARG),
     (dict(N=0), B.FA_ERR_INVALID_ARG),
+    (dict(B=1, H=1, N=1 << 24), B.FA_ERR_INVALID_ARG),
     (dict(scale=float("nan")), B.FA_ERR_INVALID_ARG),
     (dict(causal=-1), B.FA_ERR_INVALID_ARG),
     (dict(g_dtype=5), B.FA_ERR_INVALID_ARG),
@@ -232,6 +236,7 @@ def dec(**kw):
     (dict(ws=None), B.FA_ERR_WORKSPACE),
     (dict(ws_bytes=100), B.FA_ERR_WORKSPACE),
     (dict(B=1, H=1, Nk=(1 << 23) + 1), B.FA_ERR_INVALID_ARG),
+    (dict(B=1, H=1, Nk=1 << 23), B.FA_ERR_INVALID_ARG),
 ])
 def test_decode_rejects(kw, status):
     assert dec(**kw) == status
