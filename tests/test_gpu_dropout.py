@@ -251,3 +251,86 @@ def test_backward_keep_mask_bit_exact(fa, dtype, d):
                 bad = np.argwhere(got_q != want_q)
                 assert bad.size == 0, f"dQ head {(b, h)}: keep bits differ at (row, col) {bad[:5]}"
         assert np.abs(host64(dk)).max() == 0.0  # Q = 0: dK = scale * dS^T Q vanishes
+
+
+# --- full-chip grids --------------------------------------------------------------------------
+
+def _full_grid_heads(n, causal):
+    """B, H (B*H a multiple of 8) giving at least 512 causal, or 256 non-causal, 256-query tiles:
+    grids that fill the chip, where the plain forward switches to its two-group kernel."""
+    need = 512 if causal else 256
+    tiles = -(-n // 256)
+    H = 8
+    while tiles * 4 * H < need:
+        H += 8
+    return 4, H
+
+
+def _spread_heads(B, H, count=8):
+    """count (b, h) pairs spread over all B*H heads (one per XCD group of heads)."""
+    bh = B * H
+    return [divmod(i * bh // count + (i % 3), H) for i in range(count)]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [32, 64, 96])
+@pytest.mark.parametrize("causal", [False, True])
+def test_full_grid_forward_keep_mask_bit_exact(fa, dtype, d, causal):
+    """The read-out of test_forward_keep_mask_bit_exact on a full-chip grid (ragged N, 8 heads
+    spread over the grid compared bit for bit, every head finite)."""
+    import torch
+    p, seed, offset = 0.3, 0x0BAD_CAFE_1234_5678, 9
+    # Rows reach 2^((N - 1) // d): at most 2^15 keeps them finite in fp16, and the read-out
+    # integers exact in fp32.
+    n = min(1000, 16 * d - 8)
+    B, H = _full_grid_heads(n, causal)
+    print(f"  B={B} H={H} N={n}", flush=True)
+    ks32 = float(np.float32(keep_scale(p)))
+    rng = np.random.default_rng(n + d + causal)
+    qv = inp.quantize(rng.standard_normal((B, H, n, d), dtype=np.float32), dtype)
+    q = to_device(qv)
+    v = to_device(inp.quantize(np.broadcast_to(_pow2_rows(n, d), (B, H, n, d)).copy(), dtype))
+    k = torch.zeros_like(q)
+    out = nan_like((B, H, n, d), torch.float32)
+    lse = nan_like((B, H, n), torch.float32)
+    fa.forward(q, k, v, causal=causal, out=out, lse=lse, dropout_p=p, seed=seed, offset=offset)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())
+    o = host64(out)
+    vis = np.tril(np.ones((n, n), dtype=bool)) if causal else np.ones((n, n), dtype=bool)
+    l_rows = vis.sum(axis=1).astype(np.float64)
+    for (b, h) in _spread_heads(B, H):
+        z = dropout_keep_ref(n, n, b * H + h, seed, offset, p) & vis
+        got = _digits(o[b, h] * l_rows[:, None], ks32)
+        bad = np.argwhere(got != _mask_digits(z, d))
+        assert bad.size == 0, f"head {(b, h)}: keep bits differ at (row, col) {bad[:5]}"
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [32, 64, 96])
+@pytest.mark.parametrize("causal", [False, True])
+def test_full_grid_forward_dropout_parity(fa, dtype, d, causal):
+    """Random inputs on a full-chip grid with dropout: O and LSE of 8 heads spread over the grid
+    against the oracle (ragged N = 1000), every head finite."""
+    import torch
+    p, seed, offset = 0.15, 77, 4
+    n = 1000
+    B, H = _full_grid_heads(n, causal)
+    print(f"  B={B} H={H} N={n}", flush=True)
+    t = inp.draw((B, H, n, d), dtype, 5 * d + causal)
+    q, k, v = (to_device(t[nm]) for nm in ("q", "k", "v"))
+    out = nan_like((B, H, n, d), torch.float32)
+    lse = nan_like((B, H, n), torch.float32)
+    scale = 1.0 / math.sqrt(d)
+    fa.forward(q, k, v, scale=scale, causal=causal, out=out, lse=lse, dropout_p=p, seed=seed,
+               offset=offset)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())
+    ks = keep_scale(p)
+    for (b, h) in _spread_heads(B, H):
+        keep = dropout_keep_ref(n, n, b * H + h, seed, offset, p)
+        o_ref, l_ref = attn_fwd_ref(t["q"].values[b, h], t["k"].values[b, h],
+                                    t["v"].values[b, h], scale, causal, keep=keep, keep_scale=ks)
+        check("O", host64(out[b, h]), o_ref, 2e-2)
+        check("LSE", host64(lse[b, h]), l_ref, 1e-3)
+
