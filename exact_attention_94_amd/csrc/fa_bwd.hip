@@ -310,15 +310,32 @@ struct Dkdv {
   static constexpr int MASK_BYTES = 4 * BQ * 4;
 };
 
+// Groups of four waves per workgroup of the keys-outer kernel. Block-sparse instances at d <= 64
+// use two: both groups hold the tile's 128 keys and take alternate live query steps, so that a
+// mask column much denser than the others (a global key block, seen by every query block) costs
+// its workgroup half as long; the groups' dK and dV are added in a fixed order through LDS at
+// the end.
+template <int D, bool SPARSE>
+constexpr int dkdv_groups() {
+  return (SPARSE && D <= 64) ? 2 : 1;
+}
+
 template <int D, bool IS_BF16, bool G_F32, bool CAUSAL, bool DROP, bool SPARSE>
-__global__ __launch_bounds__(256, (D <= 64 ? kDkdvWaves64 : 1)) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__((256 * dkdv_groups<D, SPARSE>()), (D <= 64 ? kDkdvWaves64 : 1))
+void bwd_dkdv_kernel(BwdArgs a) {
   using C = Dkdv<D, dkdv_bq<D, IS_BF16, CAUSAL, SPARSE>()>;
+  constexpr int NG = dkdv_groups<D, SPARSE>();
   static_assert(!(DROP && SPARSE), "the dropout words and the sparse list share one LDS area");
+  static_assert(NG == 1 || 4 * 2 * C::DB * 16 * 64 * 4 <= NG * C::LDS_BYTES,
+                "the second group's dK / dV fit the stages for the final sum");
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
+  // Wave-uniform (scalar) indices: group gi, wave within the group.
+  const int gi = NG == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 8);
+  const int wave = __builtin_amdgcn_readfirstlane(NG == 1 ? tid >> 6 : (tid >> 6) & 3);
+  uint16_t* const gsm = smem + gi * 2 * C::STAGE;  // this group's two stages
   const int g = lane >> 5;
   const int r = lane & 31;
   const int N = a.N;    // query rows
@@ -357,7 +374,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? kDkdvWaves64 : 1)) void bwd_dkdv_ke
       kf[ks].w = to_f16x8<true>(kf[ks].w);
       vf[ks].w = to_f16x8<true>(vf[ks].w);
     }
-    if (key < Nk) {
+    if (gi == 0 && key < Nk) {  // one copy per key (both groups hold the same keys)
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
         const size_t off = kv_off + (size_t)key * D + ks * 16 + g * 8;
@@ -390,7 +407,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? kDkdvWaves64 : 1)) void bwd_dkdv_ke
   const uint16_t* live_list = nullptr;
   if constexpr (SPARSE) {
     static_assert(C::BKV == kSparseBlock && 2 * C::BQ == kSparseBlock, "tile / block mismatch");
-    uint16_t* list = smem + 2 * C::STAGE;
+    uint16_t* list = smem + NG * 2 * C::STAGE;
     const uint8_t* mcol = a.sparse.mask +
         (size_t)(a.sparse.mask_heads == 1 ? 0 : bh) * a.sparse.nb * a.sparse.nb + kt;
     const int nb = a.sparse.nb;
@@ -421,7 +438,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? kDkdvWaves64 : 1)) void bwd_dkdv_ke
   }
   float lreg, dreg;
   auto issue_tile = [&](int stage, int i0) {
-    uint16_t* qs = smem + stage * C::STAGE;
+    uint16_t* qs = gsm + stage * C::STAGE;
     uint16_t* os = qs + C::TILE;
     const uint32_t base = (uint32_t)i0 * D * 2;
 #pragma unroll
@@ -435,7 +452,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? kDkdvWaves64 : 1)) void bwd_dkdv_ke
   };
   // After the loads of issue_tile have completed: the row vectors of the step.
   auto store_vec = [&](int stage, int i0) {
-    float* vec = reinterpret_cast<float*>(smem + stage * C::STAGE + 2 * C::TILE);
+    float* vec = reinterpret_cast<float*>(gsm + stage * C::STAGE + 2 * C::TILE);
     if (wave == 0) {
       // Rows beyond N, and rows that saw no key (LSE = -inf, block-sparse only), get +inf, so
       // that P = 0 there.
@@ -450,7 +467,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? kDkdvWaves64 : 1)) void bwd_dkdv_ke
   auto step_math = [&](int stage, int i0) {
     const bool live = (i0 < N) && (!CAUSAL || (i0 + C::BQ - 1 + qoff >= kw0));
     if (!live) return;
-    const uint16_t* qs = smem + stage * C::STAGE;
+    const uint16_t* qs = gsm + stage * C::STAGE;
     const uint16_t* os = qs + C::TILE;
     const float* lse_s = reinterpret_cast<const float*>(qs + 2 * C::TILE);
     const float* del_s = lse_s + C::BQ;
@@ -511,7 +528,7 @@ __global__ __launch_bounds__(256, (D <= 64 ? kDkdvWaves64 : 1)) void bwd_dkdv_ke
       for (int kg = 0; kg < 4; ++kg)
         word |= keep_bits8(a.drop, (uint32_t)(kw0 >> 3) + kg, (uint32_t)(i0 + lane), (uint32_t)bh)
                 << (8 * kg);
-      mask_w = reinterpret_cast<uint32_t*>(smem + 2 * C::STAGE) + wave * C::BQ;
+      mask_w = reinterpret_cast<uint32_t*>(smem + NG * 2 * C::STAGE) + wave * C::BQ;
       mask_w[lane] = word;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -585,26 +602,55 @@ __global__ __launch_bounds__(256, (D <= 64 ? kDkdvWaves64 : 1)) void bwd_dkdv_ke
   // step then starts the loads of the next tile into the other stage (whose previous tile's math
   // ended before the last barrier), does its math, waits for the loads and publishes the tile.
   // Tiles past N read zeros; their math is skipped.
-  issue_tile(0, step_i0(0));
+  // With two groups, group gi takes live steps gi, gi + 2, ...; both run n_it iterations with the
+  // same barriers (a step past the last live one maps past N: its loads read zeros, its math is
+  // skipped).
+  const int n_it = (n_live + NG - 1) / NG;
+  auto gstep = [&](int n) { return step_i0(n * NG + gi); };
+  issue_tile(0, gstep(0));
   wait_vmem_all();
-  store_vec(0, step_i0(0));
+  store_vec(0, gstep(0));
   __syncthreads();
   // Nothing is loaded or waited for after the last step.
-  for (int step = 0; step < n_live; step += 2) {
-    const bool more1 = step + 1 < n_live;
-    if (more1) issue_tile(1, step_i0(step + 1));
-    step_math(0, step_i0(step));
+  for (int step = 0; step < n_it; step += 2) {
+    const bool more1 = step + 1 < n_it;
+    if (more1) issue_tile(1, gstep(step + 1));
+    step_math(0, gstep(step));
     if (!more1) break;
     wait_vmem_all();
-    store_vec(1, step_i0(step + 1));
+    store_vec(1, gstep(step + 1));
     __syncthreads();
-    const bool more2 = step + 2 < n_live;
-    if (more2) issue_tile(0, step_i0(step + 2));
-    step_math(1, step_i0(step + 1));
+    const bool more2 = step + 2 < n_it;
+    if (more2) issue_tile(0, gstep(step + 2));
+    step_math(1, gstep(step + 1));
     if (!more2) break;
     wait_vmem_all();
-    store_vec(0, step_i0(step + 2));
+    store_vec(0, gstep(step + 2));
     __syncthreads();
+  }
+  if constexpr (NG == 2) {
+    // Group 1 hands its dK / dV to group 0 through the (now idle) stages: element (wave, block
+    // j, slot i) of lane l at float ((wave * 2 DB + j) * 16 + i) * 64 + l, j < DB for dK.
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(smem);
+    if (gi == 1) {
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          red[((wave * 2 * C::DB + db) * 16 + i) * 64 + lane] = dkacc[db][i];
+          red[((wave * 2 * C::DB + C::DB + db) * 16 + i) * 64 + lane] = dvacc[db][i];
+        }
+    }
+    __syncthreads();
+    if (gi == 1) return;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        dkacc[db][i] += red[((wave * 2 * C::DB + db) * 16 + i) * 64 + lane];
+        dvacc[db][i] += red[((wave * 2 * C::DB + C::DB + db) * 16 + i) * 64 + lane];
+      }
   }
 
   // Epilogue: dK = scale * 2^-s (dK^T acc), dV = 2^-s (dV^T acc), 2^-s undoing the head's dO
@@ -893,11 +939,12 @@ static hipError_t launch_pre(const BwdArgs& a, bool o_f32, hipStream_t s) {
 }
 
 template <typename K>
-static hipError_t launch_dyn(K kern, int grid, int lds, BwdArgs a, hipStream_t s) {
+static hipError_t launch_dyn(K kern, int grid, int lds, BwdArgs a, hipStream_t s,
+                             int threads = 256) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, a);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -909,9 +956,10 @@ static hipError_t launch_grads(BwdArgs a, hipStream_t s, hipEvent_t ev_before,
   using KV = Dkdv<D, dkdv_bq<D, IS_BF16, CAUSAL, SPARSE>()>;
   using QT = Dq<D, dq_bc<D, IS_BF16, CAUSAL, SPARSE>()>;
   a.n_tiles = (a.Nk + KV::BKV - 1) / KV::BKV;
+  constexpr int NG = dkdv_groups<D, SPARSE>();
   e = launch_dyn(bwd_dkdv_kernel<D, IS_BF16, G_F32, CAUSAL, DROP, SPARSE>, a.n_tiles * a.bh,
-                 KV::LDS_BYTES + (DROP ? KV::MASK_BYTES : 0) + (SPARSE ? kSparseListBytes : 0),
-                 a, s);
+                 NG * KV::LDS_BYTES + (DROP ? KV::MASK_BYTES : 0) + (SPARSE ? kSparseListBytes : 0),
+                 a, s, 256 * NG);
   if (e != hipSuccess) return e;
   if (ev_after && (e = hipEventRecord(ev_after, s)) != hipSuccess) return e;
   a.n_tiles = (a.N + QT::BR - 1) / QT::BR;

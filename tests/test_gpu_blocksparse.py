@@ -97,7 +97,10 @@ def test_all_live_mask_is_bitwise_the_plain_path(fa):
     """With every block live the block-sparse kernels visit the same tiles in the same order as
     the plain ones. The forward is compared at d = 128, where the plain forward also uses 64-key
     tiles (its tuned tile width at d = 64 is 128 keys); the backward at d = 64 and 128, from the
-    same O and LSE."""
+    same O and LSE. At d = 64 the block-sparse keys-outer kernel splits each key tile's query
+    steps between two groups of waves and adds the two partial dK / dV at the end, so there dK
+    and dV agree with the plain path to fp32 summation order only (bound 1e-5, far below the 2e-2
+    oracle tolerance); dQ stays bitwise."""
     import torch
     for d in (64, 128):
         t = inp.draw((2, 2, 600, d), "bf16", 12 + d, with_do=True)
@@ -113,8 +116,14 @@ def test_all_live_mask_is_bitwise_the_plain_path(fa):
             torch.cuda.synchronize()
             if d == 128:
                 assert torch.equal(o0, o1) and torch.equal(l0, l1)
-            for x, y in zip(g0, g1):
-                assert torch.equal(x, y)
+            for name, x, y in zip(("dQ", "dK", "dV"), g0, g1):
+                if d == 64 and name != "dQ":
+                    diff = float((x - y).abs().max())
+                    print(f"  d={d} causal={causal} {name}: max |plain - sparse| = {diff:.3e}",
+                          flush=True)
+                    assert diff <= 1e-5, (name, diff)
+                else:
+                    assert torch.equal(x, y), name
 
 
 def test_local_global_pattern_b2h16n4k(fa):
