@@ -601,11 +601,9 @@ def main():
         ev.record(ef0[i], stream)
         fa.forward(q, k, v, scale=w.scale, causal=True, out=o, lse=lse)
         ev.record(ef1[i], stream)
-        fa.binding.profile_backward_main(eb0[i], eb1[i])
         fa.backward(q, k, v, o, do, lse, scale=w.scale, causal=True, grad_dtype=torch.float32,
-                    workspace=ws, grads=grads)
+                    workspace=ws, grads=grads, main_events=(eb0[i], eb1[i]))
         ev.record(eb2[i], stream)
-    fa.binding.profile_backward_main(None, None)
     torch.cuda.synchronize()
 
     fwd_ms = sum(ev.ms(ef0[i], ef1[i]) for i in range(K)) / K

@@ -22,7 +22,7 @@ EXPORTS = ("fa_forward", "fa_forward_dropout", "fa_forward_blocksparse", "fa_for
            "fa_backward", "fa_backward_kv", "fa_backward_kv_workspace_bytes",
            "fa_backward_dropout", "fa_backward_blocksparse", "fa_backward_workspace_bytes",
            "fa_decode_workspace_bytes", "fa_decode_forward", "fa_decode_forward_noalloc",
-           "fa_profile_backward_main", "fa_status_string")
+           "fa_backward_timed", "fa_status_string")
 
 DECODE_SCRATCH_BYTES = 8 << 20  # FA_DECODE_SCRATCH_BYTES
 
@@ -83,8 +83,9 @@ def load(path=LIB_PATH):
     lib.fa_decode_forward.restype = i
     lib.fa_decode_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp]
     lib.fa_decode_forward_noalloc.restype = i
-    lib.fa_profile_backward_main.argtypes = [vp, vp]
-    lib.fa_profile_backward_main.restype = i
+    lib.fa_backward_timed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i,
+                                      i, vp, sz, vp, vp, vp]
+    lib.fa_backward_timed.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -195,20 +196,12 @@ def forward(q, k, v, scale=None, causal=False, o_dtype=None, out=None, lse=None,
     return out, lse
 
 
-def profile_backward_main(before, after):
-    """Ask this thread's fa_backward calls to record two hipEvent_t handles (ints) around the main
-    backward kernel; (None, None) stops."""
-    st = load().fa_profile_backward_main(before, after)
-    if st != FA_OK:
-        raise FAError(st, "fa_profile_backward_main")
-
-
 def workspace_bytes(B, H, N, d, in_dtype_code, grad_dtype_code):
     return int(load().fa_backward_workspace_bytes(B, H, N, d, in_dtype_code, grad_dtype_code))
 
 
 def backward(q, k, v, o, dout, lse, scale=None, causal=False, grad_dtype=None, workspace=None,
-             grads=None, dropout_p=None, seed=0, offset=0, block_mask=None):
+             grads=None, dropout_p=None, seed=0, offset=0, block_mask=None, main_events=None):
     """fa_backward on torch tensors. Returns (dQ, dK, dV) in grad_dtype (default: q.dtype).
 
     `workspace` (a uint8 GPU tensor) is allocated when not given; `grads` may supply the three
@@ -216,7 +209,8 @@ def backward(q, k, v, o, dout, lse, scale=None, causal=False, grad_dtype=None, w
     the forward's keep mask from the same (dropout_p, seed, offset); with block_mask it is
     fa_backward_blocksparse (the mask given to the forward). If k and v have another length Nk
     than q, the call is fa_backward_kv (the backward of fa_forward_kv); dK and dV are then
-    [B, H, Nk, d].
+    [B, H, Nk, d]. main_events (two hipEvent_t handles as ints; plain attention only) makes the
+    call fa_backward_timed, which records them around the dK/dV kernel.
     """
     torch = _torch()
     for name, t in (("q", q), ("o", o), ("dout", dout)):
@@ -250,6 +244,14 @@ def backward(q, k, v, o, dout, lse, scale=None, causal=False, grad_dtype=None, w
             int(bool(causal)), dtype_code(q.dtype), dtype_code(o.dtype), gcode)
     if dropout_p is not None and block_mask is not None:
         raise ValueError("dropout and a block mask cannot be combined")
+    if main_events is not None:
+        if Nk != N or dropout_p is not None or block_mask is not None:
+            raise ValueError("main_events times plain self-attention only")
+        st = load().fa_backward_timed(*args, workspace.data_ptr(), workspace.numel(), _stream(q),
+                                      int(main_events[0]), int(main_events[1]))
+        if st != FA_OK:
+            raise FAError(st, "fa_backward_timed")
+        return dq, dk, dv
     if Nk != N:
         if dropout_p is not None or block_mask is not None:
             raise ValueError("dropout and block masks need Nk = Nq")

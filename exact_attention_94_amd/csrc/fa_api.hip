@@ -37,10 +37,6 @@ float log2_scale(float scale) {
   return c == 0.f ? 1e-30f : c;
 }
 
-// Events the calling thread asked fa_backward to record around its main kernel.
-thread_local hipEvent_t t_prof_before = nullptr;
-thread_local hipEvent_t t_prof_after = nullptr;
-
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Dropout parameters: keep threshold T = floor((1 - p) * 65536 + 1/2) over 16-bit random values
@@ -198,7 +194,8 @@ fa_status backward_impl(const void* q, const void* k, const void* v, const void*
                         int H, int N, int d, float scale, int causal, fa_dtype in_dtype,
                         fa_dtype o_dtype, fa_dtype grad_dtype, const fa::DropParams* drop,
                         const fa::SparseParams* sparse, void* workspace, size_t workspace_bytes,
-                        void* stream, int Nk = 0) {
+                        void* stream, int Nk = 0, hipEvent_t ev_before = nullptr,
+                        hipEvent_t ev_after = nullptr) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
       !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
@@ -281,7 +278,7 @@ fa_status backward_impl(const void* q, const void* k, const void* v, const void*
       in_dtype == FA_F32
           ? fa::launch_backward_f32(a, d, causal != 0, hs)
           : fa::launch_backward(a, d, (int)in_dtype, (int)o_dtype, (int)grad_dtype, causal != 0,
-                                mode, hs, t_prof_before, t_prof_after);
+                                mode, hs, ev_before, ev_after);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -482,11 +479,17 @@ fa_status fa_decode_forward_noalloc(const void* q, const void* k, const void* v,
                            ws, L.total, stream);
 }
 
-fa_status fa_profile_backward_main(void* before, void* after) {
-  if ((before == nullptr) != (after == nullptr)) return FA_ERR_INVALID_ARG;
-  t_prof_before = static_cast<hipEvent_t>(before);
-  t_prof_after = static_cast<hipEvent_t>(after);
-  return FA_OK;
+fa_status fa_backward_timed(const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                            int B, int H, int N, int d, float scale, int causal,
+                            fa_dtype in_dtype, fa_dtype o_dtype, fa_dtype grad_dtype,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            void* ev_before, void* ev_after) {
+  if (!ev_before || !ev_after) return FA_ERR_INVALID_ARG;
+  if (in_dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, in_dtype,
+                       o_dtype, grad_dtype, nullptr, nullptr, workspace, workspace_bytes, stream,
+                       0, static_cast<hipEvent_t>(ev_before), static_cast<hipEvent_t>(ev_after));
 }
 
 }  // extern "C"

@@ -105,8 +105,9 @@ def _declare(lib):
     lib.fa_backward.restype = i
     lib.fa_backward_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_backward_workspace_bytes.restype = sz
-    lib.fa_profile_backward_main.argtypes = [vp, vp]
-    lib.fa_profile_backward_main.restype = i
+    lib.fa_backward_timed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i,
+                                      i, vp, sz, vp, vp, vp]
+    lib.fa_backward_timed.restype = i
 
 
 def _time_key(lib, ev, d, dtype, causal, steps=10, warmup=3):
@@ -133,11 +134,14 @@ def _time_key(lib, ev, d, dtype, causal, steps=10, warmup=3):
         if st != 0:
             raise RuntimeError(f"fa_forward returned {st}")
 
-    def bwd():
-        st = lib.fa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                             do.data_ptr(), lse.data_ptr(), grads[0].data_ptr(),
-                             grads[1].data_ptr(), grads[2].data_ptr(), B, H, N, d, d ** -0.5, c,
-                             code, 0, 0, ws.data_ptr(), ws.numel(), stream)
+    def bwd(ev0=None, ev1=None):
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                lse.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(), B,
+                H, N, d, d ** -0.5, c, code, 0, 0, ws.data_ptr(), ws.numel(), stream)
+        if ev0 is None:
+            st = lib.fa_backward(*args)
+        else:  # the same computation, with events around the dK/dV kernel
+            st = lib.fa_backward_timed(*args, ev0, ev1)
         if st != 0:
             raise RuntimeError(f"fa_backward returned {st}")
 
@@ -150,10 +154,8 @@ def _time_key(lib, ev, d, dtype, causal, steps=10, warmup=3):
         ev.record(e[i][0], stream)
         fwd()
         ev.record(e[i][1], stream)
-        lib.fa_profile_backward_main(e[i][2], e[i][3])
-        bwd()
+        bwd(e[i][2], e[i][3])
         ev.record(e[i][4], stream)
-    lib.fa_profile_backward_main(None, None)
     torch.cuda.synchronize()
     med = lambda xs: sorted(xs)[len(xs) // 2]  # noqa: E731
     return (med([ev.ms(x[0], x[1]) for x in e]), med([ev.ms(x[1], x[4]) for x in e]),

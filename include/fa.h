@@ -285,13 +285,20 @@ fa_status fa_decode_forward_noalloc(const void* q, const void* k, const void* v,
                                     void* stream);
 
 /*
- * Profiling aid with no effect on results: after this call, every fa_backward call made by the
- * calling thread records `before` on its stream immediately before its dK/dV kernel (the
- * longest of its kernels) is launched and `after` immediately after it, so the caller can time
- * that kernel alone with hipEventElapsedTime. Both are hipEvent_t handles owned by the caller. Pass NULL, NULL to stop.
- * Returns FA_ERR_INVALID_ARG if exactly one of them is NULL, FA_OK otherwise.
+ * fa_backward with a measurement aid that leaves the results unchanged (the same kernels and
+ * arithmetic as fa_backward on the same arguments). It records `ev_before` on `stream` right
+ * before the dK/dV kernel is launched and `ev_after` right after it. The caller can then time
+ * that kernel, the longest of the backward, with hipEventElapsedTime. Both are hipEvent_t handles
+ * the caller owns; the library keeps no reference to them after the call.
+ * 16-bit inputs only (FA_F32 returns FA_ERR_UNSUPPORTED). A NULL event returns
+ * FA_ERR_INVALID_ARG. Other arguments and errors are as for fa_backward.
  */
-fa_status fa_profile_backward_main(void* before, void* after);
+fa_status fa_backward_timed(const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                            int B, int H, int N, int d, float scale, int causal,
+                            fa_dtype in_dtype, fa_dtype o_dtype, fa_dtype grad_dtype,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            void* ev_before, void* ev_after);
 
 /* A static, human-readable description of a status code (never NULL). */
 const char* fa_status_string(fa_status s);

@@ -194,9 +194,16 @@ int main(void) {
                                    FA_BF16, NULL),
          FA_ERR_INVALID_ARG);
 
-  /* Profiling hook. */
-  EXPECT(fa_profile_backward_main(P, NULL), FA_ERR_INVALID_ARG);
-  EXPECT(fa_profile_backward_main(NULL, NULL), FA_OK);
+  /* Timed backward: both events required, 16-bit inputs only, then fa_backward's checks. */
+  EXPECT(fa_backward_timed(P, P, P, P, P, FP, P, P, P, 2, 3, 100, 64, 0.125f, 1, FA_BF16, FA_F32,
+                           FA_F32, P, (size_t)1 << 30, NULL, P, NULL),
+         FA_ERR_INVALID_ARG);
+  EXPECT(fa_backward_timed(P, P, P, P, P, FP, P, P, P, 2, 3, 100, 64, 0.125f, 1, FA_F32, FA_F32,
+                           FA_F32, P, (size_t)1 << 30, NULL, P, P),
+         FA_ERR_UNSUPPORTED);
+  EXPECT(fa_backward_timed(P, P, P, P, P, FP, P, P, P, 2, 3, 100, 64, 0.125f, 1, FA_BF16, FA_F32,
+                           FA_F32, NULL, 0, NULL, P, P),
+         FA_ERR_WORKSPACE);
 
   if (failures) {
     fprintf(stderr, "%d of %d checks failed\n", failures, checks);

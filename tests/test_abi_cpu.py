@@ -383,11 +383,28 @@ def test_product_path_never_touches_the_oracle():
                     os.path.join(dirpath, f)
 
 
-def test_profile_hook_argument_check():
-    lib = _lib()
-    assert lib.fa_profile_backward_main(P, None) == B.FA_ERR_INVALID_ARG
-    assert lib.fa_profile_backward_main(None, P) == B.FA_ERR_INVALID_ARG
-    assert lib.fa_profile_backward_main(None, None) == B.FA_OK
+def bwd_timed(ev0=P, ev1=P, **kw):
+    a = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=2, H=3, N=100, d=64,
+             scale=0.125, causal=1, in_dtype=B.FA_BF16, o_dtype=B.FA_F32, g_dtype=B.FA_F32,
+             ws=P, ws_bytes=1 << 30)
+    a.update(kw)
+    return _lib().fa_backward_timed(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"],
+                                    a["dk"], a["dv"], a["B"], a["H"], a["N"], a["d"],
+                                    a["scale"], a["causal"], a["in_dtype"], a["o_dtype"],
+                                    a["g_dtype"], a["ws"], a["ws_bytes"], None, ev0, ev1)
+
+
+def test_timed_backward_rejects_before_any_hip_call():
+    """fa_backward_timed needs both events, takes 16-bit inputs only, and otherwise validates
+    exactly like fa_backward (every case below returns before a HIP call or launch)."""
+    assert bwd_timed(ev0=None) == B.FA_ERR_INVALID_ARG
+    assert bwd_timed(ev1=None) == B.FA_ERR_INVALID_ARG
+    assert bwd_timed(in_dtype=B.FA_F32, o_dtype=B.FA_F32) == B.FA_ERR_UNSUPPORTED
+    assert bwd_timed(N=0) == B.FA_ERR_INVALID_ARG
+    assert bwd_timed(dq=None) == B.FA_ERR_INVALID_ARG
+    assert bwd_timed(d=80) == B.FA_ERR_UNSUPPORTED
+    assert bwd_timed(ws=None) == B.FA_ERR_WORKSPACE
+    assert bwd_timed(ws_bytes=16) == B.FA_ERR_WORKSPACE
 
 
 def test_decode_noalloc_rejects():
