@@ -280,11 +280,12 @@ __device__ __forceinline__ void store_grad4(void* base, size_t off, float x0, fl
 // 2. dK / dV: keys outer.
 // ----------------------------------------------------------------------------------------
 // Queries per step of the keys-outer kernel and keys per tile of the queries-outer kernel: from
-// the tuning table for plain attention and dropout, 64 for block-sparse masks (half a mask
-// block).
-template <int D, bool IS_BF16, bool CAUSAL, bool SPARSE>
+// the tuning table for plain attention (and, for the queries-outer kernel, dropout); 64 for
+// block-sparse masks (half a mask block) and for the keys-outer kernel with dropout, whose keep
+// words take the registers that 32-query steps would give to a third wave per SIMD.
+template <int D, bool IS_BF16, bool CAUSAL, bool SPARSE, bool DROP = false>
 constexpr int dkdv_bq() {
-  return SPARSE ? 64 : dkdv_step_queries<D, IS_BF16, CAUSAL>();
+  return (SPARSE || DROP) ? 64 : dkdv_step_queries<D, IS_BF16, CAUSAL>();
 }
 template <int D, bool IS_BF16, bool CAUSAL, bool SPARSE>
 constexpr int dq_bc() {
@@ -321,9 +322,10 @@ constexpr int dkdv_groups() {
 }
 
 template <int D, bool IS_BF16, bool G_F32, bool CAUSAL, bool DROP, bool SPARSE>
-__global__ __launch_bounds__((256 * dkdv_groups<D, SPARSE>()), (D <= 64 ? kDkdvWaves64 : 1))
+__global__ __launch_bounds__((256 * dkdv_groups<D, SPARSE>()),
+                             (dkdv_waves<D, dkdv_bq<D, IS_BF16, CAUSAL, SPARSE, DROP>(), DROP>()))
 void bwd_dkdv_kernel(BwdArgs a) {
-  using C = Dkdv<D, dkdv_bq<D, IS_BF16, CAUSAL, SPARSE>()>;
+  using C = Dkdv<D, dkdv_bq<D, IS_BF16, CAUSAL, SPARSE, DROP>()>;
   constexpr int NG = dkdv_groups<D, SPARSE>();
   static_assert(!(DROP && SPARSE), "the dropout words and the sparse list share one LDS area");
   static_assert(NG == 1 || 4 * 2 * C::DB * 16 * 64 * 4 <= NG * C::LDS_BYTES,
@@ -494,8 +496,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
           }
       }
     }
-    // Fragment f = (ks, qb, tensor: Q for S, dO for dP), read dkdv_pre<D>() ahead of its MFMA.
-    read_ahead<2 * C::KS * C::QBS, dkdv_pre<D>()>(
+    // Fragment f = (ks, qb, tensor: Q for S, dO for dP), read dkdv_pre<D, BQ>() ahead of its MFMA.
+    read_ahead<2 * C::KS * C::QBS, dkdv_pre<D, C::BQ>()>(
         [&](int f) {
           const int ks = f / (2 * C::QBS), qb = (f / 2) % C::QBS;
           const uint16_t* src = (f & 1) ? os : qs;
@@ -953,7 +955,7 @@ static hipError_t launch_grads(BwdArgs a, hipStream_t s, hipEvent_t ev_before,
                                hipEvent_t ev_after) {
   hipError_t e;
   if (ev_before && (e = hipEventRecord(ev_before, s)) != hipSuccess) return e;
-  using KV = Dkdv<D, dkdv_bq<D, IS_BF16, CAUSAL, SPARSE>()>;
+  using KV = Dkdv<D, dkdv_bq<D, IS_BF16, CAUSAL, SPARSE, DROP>()>;
   using QT = Dq<D, dq_bc<D, IS_BF16, CAUSAL, SPARSE>()>;
   a.n_tiles = (a.Nk + KV::BKV - 1) / KV::BKV;
   constexpr int NG = dkdv_groups<D, SPARSE>();

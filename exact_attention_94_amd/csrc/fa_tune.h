@@ -16,9 +16,9 @@
 // tiles (32 keys forward, 32 queries dK/dV, 32 keys dQ).
 #pragma once
 
-#define FA_FWD_BC_TABLE {{{128, 128}, {128, 128}}, {{128, 128}, {128, 128}}, {{64, 64}, {64, 64}}, {{64, 64}, {64, 64}}}
-#define FA_DKDV_BQ_TABLE {{{64, 64}, {64, 64}}, {{64, 64}, {64, 64}}, {{64, 64}, {64, 64}}, {{64, 64}, {64, 64}}}
-#define FA_DQ_BC_TABLE {{{64, 64}, {64, 64}}, {{64, 64}, {32, 64}}, {{64, 64}, {64, 64}}, {{64, 32}, {64, 32}}}
+#define FA_FWD_BC_TABLE {{{64, 128}, {64, 128}}, {{128, 128}, {128, 128}}, {{64, 64}, {64, 64}}, {{64, 64}, {64, 64}}}
+#define FA_DKDV_BQ_TABLE {{{64, 64}, {64, 64}}, {{64, 32}, {64, 32}}, {{64, 64}, {64, 64}}, {{64, 64}, {64, 64}}}
+#define FA_DQ_BC_TABLE {{{64, 64}, {64, 64}}, {{64, 64}, {64, 64}}, {{64, 64}, {64, 64}}, {{32, 32}, {32, 32}}}
 
 // LDS operand reads kept in flight ahead of the MFMAs of the score products (forward S, and S
 // with dP in both backward kernels); overridable with -DFA_FWD_PRE / -DFA_DKDV_PRE / -DFA_DQ_PRE.
@@ -27,6 +27,11 @@
 #endif
 #ifndef FA_DKDV_PRE
 #define FA_DKDV_PRE 4
+#endif
+// The same for 32-query steps of the dK/dV kernel, which run three waves per SIMD (fewer
+// registers for fragments in flight).
+#ifndef FA_DKDV_PRE_32
+#define FA_DKDV_PRE_32 2
 #endif
 #ifndef FA_DQ_PRE
 #define FA_DQ_PRE 4
@@ -37,9 +42,14 @@
 #ifndef FA_FWD_PP_MIN_BLOCKS
 #define FA_FWD_PP_MIN_BLOCKS 512
 #endif
-// Waves per SIMD the dK/dV kernel's register allocation must allow at d <= 64.
+// Waves per SIMD the dK/dV kernel's register allocation must allow at d <= 64: with 64-query
+// steps, and with 32-query steps of plain attention (whose score and dP blocks take half the
+// registers).
 #ifndef FA_DKDV_WAVES_64
 #define FA_DKDV_WAVES_64 2
+#endif
+#ifndef FA_DKDV_WAVES_64_BQ32
+#define FA_DKDV_WAVES_64_BQ32 3
 #endif
 // Waves per SIMD the dQ kernel's register allocation must allow at d <= 64.
 #ifndef FA_DQ_WAVES_64
@@ -54,9 +64,9 @@ template <int D>
 constexpr int fwd_pre() {
   return D == 64 ? FA_FWD_PRE : 0;
 }
-template <int D>
+template <int D, int BQ>
 constexpr int dkdv_pre() {
-  return D == 64 ? FA_DKDV_PRE : 0;
+  return D == 64 ? (BQ == 32 ? FA_DKDV_PRE_32 : FA_DKDV_PRE) : 0;
 }
 template <int D>
 constexpr int dq_pre() {
@@ -64,6 +74,12 @@ constexpr int dq_pre() {
 }
 constexpr int kDqWaves64 = FA_DQ_WAVES_64;
 constexpr int kDkdvWaves64 = FA_DKDV_WAVES_64;
+// Waves per SIMD of the dK/dV kernel (launch bound): d <= 64 as above (dropout keeps the 64-query
+// budget: its keep words need the registers), one wave at larger head dims.
+template <int D, int BQ, bool DROP>
+constexpr int dkdv_waves() {
+  return D > 64 ? 1 : (BQ == 32 && !DROP) ? FA_DKDV_WAVES_64_BQ32 : FA_DKDV_WAVES_64;
+}
 constexpr int kFwdPpMinBlocks = FA_FWD_PP_MIN_BLOCKS;
 
 constexpr int kFwdBcTable[4][2][2] = FA_FWD_BC_TABLE;
