@@ -697,8 +697,9 @@ struct Dq {
 };
 
 template <int D, bool IS_BF16, bool G_F32, bool CAUSAL, bool DROP, bool SPARSE>
-__global__ __launch_bounds__(256, (D <= 64 ? kDqWaves64 : D <= 128 ? 2 : 1)) void bwd_dq_kernel(
-    BwdArgs a) {
+__global__ __launch_bounds__(256,
+                             (dq_waves<D, dq_bc<D, IS_BF16, CAUSAL, SPARSE>(), !DROP && !SPARSE>()))
+void bwd_dq_kernel(BwdArgs a) {
   using C = Dq<D, dq_bc<D, IS_BF16, CAUSAL, SPARSE>()>;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
@@ -810,8 +811,8 @@ __global__ __launch_bounds__(256, (D <= 64 ? kDqWaves64 : D <= 128 ? 2 : 1)) voi
     // end as dP^T - D.
     f32x16 sacc[C::KB], pacc[C::KB];
     const f32x16 zero16 = {};
-    // Fragment f = (ks, kb, tensor: K for S^T, V for dP^T), read dq_pre<D>() ahead of its MFMA.
-    read_ahead<2 * C::KS * C::KB, dq_pre<D>()>(
+    // Fragment f = (ks, kb, tensor: K for S^T, V for dP^T), read dq_pre<D, BC>() ahead of its MFMA.
+    read_ahead<2 * C::KS * C::KB, dq_pre<D, C::BC>()>(
         [&](int f) {
           const int ks = f / (2 * C::KB), kb = (f / 2) % C::KB;
           const uint16_t* src = (f & 1) ? vs_ : ks_;

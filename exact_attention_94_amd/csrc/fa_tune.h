@@ -18,7 +18,7 @@
 
 #define FA_FWD_BC_TABLE {{{64, 128}, {64, 128}}, {{128, 128}, {128, 128}}, {{64, 64}, {64, 64}}, {{64, 64}, {64, 64}}}
 #define FA_DKDV_BQ_TABLE {{{64, 64}, {64, 64}}, {{64, 32}, {64, 32}}, {{64, 64}, {64, 64}}, {{64, 64}, {64, 64}}}
-#define FA_DQ_BC_TABLE {{{64, 64}, {64, 64}}, {{64, 64}, {64, 64}}, {{64, 64}, {64, 64}}, {{32, 32}, {32, 32}}}
+#define FA_DQ_BC_TABLE {{{64, 64}, {64, 64}}, {{64, 32}, {64, 32}}, {{64, 64}, {64, 64}}, {{32, 32}, {32, 32}}}
 
 // LDS operand reads kept in flight ahead of the MFMAs of the score products (forward S, and S
 // with dP in both backward kernels); overridable with -DFA_FWD_PRE / -DFA_DKDV_PRE / -DFA_DQ_PRE.
@@ -36,6 +36,10 @@
 #ifndef FA_DQ_PRE
 #define FA_DQ_PRE 4
 #endif
+// The same for 32-key tiles of the dQ kernel, which run three waves per SIMD.
+#ifndef FA_DQ_PRE_32
+#define FA_DQ_PRE_32 0
+#endif
 // Fewest workgroups for which causal plain attention runs the two-group forward kernel (256
 // queries per workgroup; half as many suffice without a causal mask); smaller grids run the
 // single-group kernel (128 queries per workgroup).
@@ -51,9 +55,13 @@
 #ifndef FA_DKDV_WAVES_64_BQ32
 #define FA_DKDV_WAVES_64_BQ32 3
 #endif
-// Waves per SIMD the dQ kernel's register allocation must allow at d <= 64.
+// Waves per SIMD the dQ kernel's register allocation must allow at d <= 64: with 64-key tiles,
+// and with 32-key tiles of plain attention.
 #ifndef FA_DQ_WAVES_64
 #define FA_DQ_WAVES_64 2
+#endif
+#ifndef FA_DQ_WAVES_64_BC32
+#define FA_DQ_WAVES_64_BC32 3
 #endif
 
 namespace fa {
@@ -68,11 +76,17 @@ template <int D, int BQ>
 constexpr int dkdv_pre() {
   return D == 64 ? (BQ == 32 ? FA_DKDV_PRE_32 : FA_DKDV_PRE) : 0;
 }
-template <int D>
+template <int D, int BC>
 constexpr int dq_pre() {
-  return D == 64 ? FA_DQ_PRE : 0;
+  return D == 64 ? (BC == 32 ? FA_DQ_PRE_32 : FA_DQ_PRE) : 0;
 }
 constexpr int kDqWaves64 = FA_DQ_WAVES_64;
+// Waves per SIMD of the dQ kernel (launch bound): d <= 64 as above (dropout and block masks keep
+// two), two at d = 96 and 128, one at d = 256.
+template <int D, int BC, bool PLAIN>
+constexpr int dq_waves() {
+  return D > 128 ? 1 : D > 64 ? 2 : (BC == 32 && PLAIN) ? FA_DQ_WAVES_64_BC32 : FA_DQ_WAVES_64;
+}
 constexpr int kDkdvWaves64 = FA_DKDV_WAVES_64;
 // Waves per SIMD of the dK/dV kernel (launch bound): d <= 64 as above (dropout keeps the 64-query
 // budget: its keep words need the registers), one wave at larger head dims.
