@@ -80,14 +80,12 @@ template <int D, int BC>
 constexpr int dq_pre() {
   return D == 64 ? (BC == 32 ? FA_DQ_PRE_32 : FA_DQ_PRE) : 0;
 }
-constexpr int kDqWaves64 = FA_DQ_WAVES_64;
 // Waves per SIMD of the dQ kernel (launch bound): d <= 64 as above (dropout and block masks keep
 // two), two at d = 96 and 128, one at d = 256.
 template <int D, int BC, bool PLAIN>
 constexpr int dq_waves() {
   return D > 128 ? 1 : D > 64 ? 2 : (BC == 32 && PLAIN) ? FA_DQ_WAVES_64_BC32 : FA_DQ_WAVES_64;
 }
-constexpr int kDkdvWaves64 = FA_DKDV_WAVES_64;
 // Waves per SIMD of the dK/dV kernel (launch bound): d <= 64 as above (dropout keeps the 64-query
 // budget: its keep words need the registers), one wave at larger head dims.
 template <int D, int BQ, bool DROP>
