@@ -513,9 +513,9 @@ def main():
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the attention path is single-GPU; see the sharding notes in DESIGN.md)",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the attention "
+              "path runs on a single GPU (heads would shard across GPUs with no communication, "
+              "but no multi-GPU path is provided)", file=sys.stderr)
         return 2
 
     import numpy as np
