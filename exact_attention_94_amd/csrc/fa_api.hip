@@ -50,6 +50,8 @@ bool make_drop(float p, uint64_t seed, uint32_t offset, fa::DropParams& dp) {
   dp.offset = offset;
   dp.keep_t = (uint32_t)t;
   dp.keep_scale = (float)(65536.0 / t);
+  dp.log2_scale = (float)log2(65536.0 / t);
+  dp.inv_scale = (float)(t / 65536.0);
   return true;
 }
 

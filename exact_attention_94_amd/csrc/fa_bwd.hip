@@ -459,8 +459,11 @@ void bwd_dkdv_kernel(BwdArgs a) {
       // Rows beyond N, and rows that saw no key (LSE = -inf, block-sparse only), get +inf, so
       // that P = 0 there.
       if (lane < C::BQ) {
-        vec[lane] = (i0 + lane < N && lreg != -INFINITY) ? lreg * kLog2e : INFINITY;
-        vec[C::BQ + lane] = -dreg;
+        // With dropout the row vectors hold LSE log2 e - log2(1/q) and -D q (q the keep rate),
+        // so that exp2 gives P / q and the dP accumulators start at -D q (see step_math).
+        const float lsh = DROP ? a.drop.log2_scale : 0.f;
+        vec[lane] = (i0 + lane < N && lreg != -INFINITY) ? lreg * kLog2e - lsh : INFINITY;
+        vec[C::BQ + lane] = DROP ? -dreg * a.drop.inv_scale : -dreg;
       }
     }
   };
@@ -475,26 +478,22 @@ void bwd_dkdv_kernel(BwdArgs a) {
     const float* del_s = lse_s + C::BQ;
 
     // S = Q K^T and dP = dO V^T (rows: queries in staged order, columns: this wave's keys).
-    // Without dropout the dP accumulators start at -D (slot i of block qb: the row vector entry
-    // of query 32qb + 16(i/8) + 8g + i%8), so that they end as dP - D; the first MFMA of each
-    // chain takes that block, or zero, as its accumulator input.
+    // The dP accumulators start at -D, with dropout -D q (slot i of block qb: the row vector
+    // entry of query 32qb + 16(i/8) + 8g + i%8), so that they end as dP - D (dP - D q); the
+    // first MFMA of each chain takes that block as its accumulator input.
     f32x16 sacc[C::QBS], pacc[C::QBS], pinit[C::QBS];
     const f32x16 zero16 = {};
 #pragma unroll
     for (int qb = 0; qb < C::QBS; ++qb) {
-      if constexpr (DROP) {
-        pinit[qb] = zero16;
-      } else {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const f32x4 v =
-                *reinterpret_cast<const f32x4*>(del_s + qb * 32 + h * 16 + g * 8 + 4 * j);
+        for (int j = 0; j < 2; ++j) {
+          const f32x4 v =
+              *reinterpret_cast<const f32x4*>(del_s + qb * 32 + h * 16 + g * 8 + 4 * j);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pinit[qb][h * 8 + 4 * j + e] = v[e];
-          }
-      }
+          for (int e = 0; e < 4; ++e) pinit[qb][h * 8 + 4 * j + e] = v[e];
+        }
     }
     // Fragment f = (ks, qb, tensor: Q for S, dO for dP), read dkdv_pre<D, BQ>() ahead of its MFMA.
     read_ahead<2 * C::KS * C::QBS, dkdv_pre<D, C::BQ>()>(
@@ -537,7 +536,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
     // P = exp2(c*S - LSE*log2e); dS = P * (dP - D). With dropout, dV takes the kept P scaled
-    // by 1 / keep rate, and dP = (dO V^T) * keep / keep rate.
+    // by 1 / keep rate, and dP = (dO V^T) * keep / keep rate; the row vectors then make exp2
+    // return P / q directly (q the keep rate).
     Frag16 pfr[C::QBS][2], dsf[C::QBS][2];
 #pragma unroll
     for (int qb = 0; qb < C::QBS; ++qb) {
@@ -546,7 +546,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
         const int qloc = qb * 32 + h * 16 + g * 8;
         const f32x4 l0 = *reinterpret_cast<const f32x4*>(lse_s + qloc);
         const f32x4 l1 = *reinterpret_cast<const f32x4*>(lse_s + qloc + 4);
-        f32x4 d0 = {}, d1 = {};  // -D (dropout only: the dP accumulators then start at zero)
+        f32x4 d0 = {}, d1 = {};  // -D q (dropout only)
         if constexpr (DROP) {
           d0 = *reinterpret_cast<const f32x4*>(del_s + qloc);
           d1 = *reinterpret_cast<const f32x4*>(del_s + qloc + 4);
@@ -563,11 +563,12 @@ void bwd_dkdv_kernel(BwdArgs a) {
           const float dv = e < 4 ? d0[e] : d1[e - 4];
           const float pv = fast_exp2(__builtin_fmaf(sacc[qb][h * 8 + e], c, -lv));
           if constexpr (DROP) {
+            // pv is P / q and the accumulator dP - D q: dS = P (dP / q - D) = pv (dP - D q)
+            // where kept, and -P D = pv (-D q) where dropped.
             const uint32_t w = e < 4 ? mw0[e] : mw1[e - 4];
             const bool keep = (w >> r) & 1u;
-            const float ks = a.drop.keep_scale;
-            p[e] = keep ? pv * ks : 0.f;
-            ds[e] = pv * ((keep ? pacc[qb][h * 8 + e] * ks : 0.f) + dv);
+            p[e] = keep ? pv : 0.f;
+            ds[e] = pv * (keep ? pacc[qb][h * 8 + e] : dv);
           } else {
             p[e] = pv;
             (void)dv;
@@ -738,9 +739,12 @@ void bwd_dq_kernel(BwdArgs a) {
   // Per-query statistics, lane-local under the transposed layout. Rows beyond N: P = 0.
   const float lse_raw = buf_ldf(lrs, (uint32_t)qrow * 4);
   const float dlt = buf_ldf(drs, (uint32_t)qrow * 4);
-  f32x16 pinit;  // initial dP^T accumulator: -D without dropout, 0 with it
+  // Initial dP^T accumulator: -D, or with dropout -D q (q the keep rate; the LSE below is then
+  // shifted by log2(1/q), so that exp2 gives P / q).
+  const float dneg = DROP ? -dlt * a.drop.inv_scale : -dlt;
+  f32x16 pinit;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) pinit[i] = DROP ? 0.f : -dlt;
+  for (int i = 0; i < 16; ++i) pinit[i] = dneg;
 
   f32x16 dqacc[C::DB];
 #pragma unroll
@@ -798,7 +802,9 @@ void bwd_dq_kernel(BwdArgs a) {
   issue_tile(0, tile_j0(0));
   wait_vmem_all();
   // Rows beyond N, and rows that saw no key (LSE = -inf, block-sparse only): P = 0.
-  const float lse2 = (qrow < N && lse_raw != -INFINITY) ? lse_raw * kLog2e : INFINITY;
+  const float lse2 = (qrow < N && lse_raw != -INFINITY)
+                         ? lse_raw * kLog2e - (DROP ? a.drop.log2_scale : 0.f)
+                         : INFINITY;
   __syncthreads();
 
   auto tile_math = [&](int stage, int j0) {
@@ -806,9 +812,9 @@ void bwd_dq_kernel(BwdArgs a) {
     if (!live) return;
     const uint16_t* ks_ = smem + stage * C::STAGE;
     const uint16_t* vs_ = ks_ + C::TILE;
-    // S^T = K Q^T and dP^T = V dO^T: rows = keys (permuted), column = this lane's query. Without
-    // dropout the dP^T chains start from the block -D of this lane's query (pinit), so that they
-    // end as dP^T - D.
+    // S^T = K Q^T and dP^T = V dO^T: rows = keys (permuted), column = this lane's query. The dP^T
+    // chains start from the block -D of this lane's query (-D q with dropout; pinit), so that
+    // they end as dP^T - D (dP^T - D q).
     f32x16 sacc[C::KB], pacc[C::KB];
     const f32x16 zero16 = {};
     // Fragment f = (ks, kb, tensor: K for S^T, V for dP^T), read dq_pre<D, BC>() ahead of its MFMA.
@@ -836,7 +842,8 @@ void bwd_dq_kernel(BwdArgs a) {
         }
     }
     // dS^T = P^T * (dP^T - D), P = exp2(c*S - LSE*log2e); with dropout dP is (dO V^T) * keep /
-    // keep rate, the keep bits of this lane's 8 keys coming from one Philox block.
+    // keep rate, the keep bits of this lane's 8 keys coming from one Philox block, and exp2
+    // returns P / q (the shifted LSE).
     Frag16 dsf[C::KB][2];
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) {
@@ -851,8 +858,9 @@ void bwd_dq_kernel(BwdArgs a) {
         for (int e = 0; e < 8; ++e) {
           const float pv = fast_exp2(__builtin_fmaf(sacc[kb][h * 8 + e], c, -lse2));
           if constexpr (DROP) {
-            const float dp = ((bits >> e) & 1u) ? pacc[kb][h * 8 + e] * a.drop.keep_scale : 0.f;
-            ds[e] = pv * (dp - dlt);
+            // pv is P / q and the accumulator dP - D q: dS = pv (dP - D q) where kept and
+            // pv (-D q) = -P D where dropped.
+            ds[e] = pv * (((bits >> e) & 1u) ? pacc[kb][h * 8 + e] : dneg);
           } else {
             ds[e] = pv * pacc[kb][h * 8 + e];
           }

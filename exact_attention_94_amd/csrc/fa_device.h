@@ -266,6 +266,8 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
 struct DropParams {
   uint32_t seed_lo, seed_hi, offset, keep_t;
   float keep_scale;  // 65536 / keep_t
+  float log2_scale;  // log2(65536 / keep_t)
+  float inv_scale;   // keep_t / 65536 (exact)
 };
 
 __device__ __forceinline__ uint32_t keep_bits8(const DropParams& dp, uint32_t group,
