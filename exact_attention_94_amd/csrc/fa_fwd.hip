@@ -293,7 +293,7 @@ __global__ __launch_bounds__(256, fwd_min_waves<D>()) void fwd16_kernel(FwdArgs 
 #pragma unroll
             for (int i = 0; i < 16; ++i) oacc[db][qb][i] *= corr;
           const float m_ref = m_run[qb];
-          float lsum = 0.f;
+          float lsum = -0.f;  // -0 + x = x exactly, so the first add folds away
 #pragma unroll
           for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
@@ -594,7 +594,7 @@ __global__ __launch_bounds__(512, 1) void fwd16pp_kernel(FwdArgs a) {
     // product, two per v_dot2c_f32_f16 in four chains; an fp16 rounding (2^-11 relative) stays
     // well inside that tolerance, and O is then normalised by the sum of exactly the weights
     // that multiplied V.
-    float lsum = 0.f;
+    float lsum = -0.f;  // -0 + x = x exactly, so the first add folds away
     float lpart[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
@@ -786,7 +786,7 @@ __global__ __launch_bounds__(256, 2) void fwd32_kernel(FwdArgs a) {
     const float corr = fast_exp2(m_run - m_new);
     m_run = m_new;
     float p[16];
-    float lsum = 0.f;
+    float lsum = -0.f;  // -0 + x = x exactly, so the first add folds away
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       p[i] = fast_exp2(__builtin_fmaf(sacc[i], c, -m_new));
