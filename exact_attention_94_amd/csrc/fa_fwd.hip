@@ -516,10 +516,10 @@ __global__ __launch_bounds__(512, 1) void fwd16pp_kernel(FwdArgs a) {
   Frag16 pf[C::KB][2];
   float corr_pend = 1.f;  // rescale factor of tile t's softmax, applied to O in its M phase
 
-  // M phase of tile t: O = corr * O + V_t P_t (V stage t % 2), then S_{t+1} (K stage (t + 1) % 2).
-  // The rescale of O sits here rather than in the softmax phase, which is the longer of the two
-  // (measured 2% faster); the order of the arithmetic on O is unchanged.
-  auto m_phase = [&](int t, int vstage, int kstage) {
+  // M phase of tile t: O = corr * O + V_t P_t (V stage t % 2), then S_{t+1} (K stage (t + 1) % 2)
+  // if t + 1 < n_s. The rescale of O sits here rather than in the softmax phase, which is the
+  // longer of the two (measured 2% faster); the order of the arithmetic on O is unchanged.
+  auto m_phase = [&](int t, int vstage, int kstage, int n_s) {
     if (t >= 0) {
       const uint16_t* vs_ = v_st + vstage * C::KTILE;
 #pragma unroll
@@ -539,7 +539,7 @@ __global__ __launch_bounds__(512, 1) void fwd16pp_kernel(FwdArgs a) {
           }
         }
     }
-    if (t + 1 < n_kt) {
+    if (t + 1 < n_s) {
       const uint16_t* ks_ = k_st + kstage * C::KTILE;
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
@@ -623,35 +623,47 @@ __global__ __launch_bounds__(512, 1) void fwd16pp_kernel(FwdArgs a) {
   wait_vmem_all();
   __syncthreads();
 
+  // Causal: group 0's queries end at qt0 + 127, so the tiles from n_math on (keys past
+  // qt0 + qoff + 127) hold no key any of its waves may see; they would leave its m, l and O
+  // unchanged. Group 0 computes only the tiles before n_math, then for the others still issues
+  // the K loads that group 1 needs and takes part in the same barriers, in the same order.
+  const int n_math = (CAUSAL && grp == 0) ? min(n_kt, (qt0 + qoff + 127) / C::BC + 1) : n_kt;
+
   if (grp == 0) {
-    m_phase(-1, 1, 0);
+    m_phase(-1, 1, 0, n_math);
     wg_barrier();
-    for (int t = 0; t < n_kt; t += 2) {
+    for (int t = 0; t < n_math; t += 2) {
       if (t + 1 < n_kt) load_k(1, t + 1);
       v_phase(t);
       wait_vmem_all();
       wg_barrier();
-      m_phase(t, 0, 1);
+      m_phase(t, 0, 1, n_math);
       wg_barrier();
-      if (t + 1 >= n_kt) break;
+      if (t + 1 >= n_math) break;
       if (t + 2 < n_kt) load_k(0, t + 2);
       v_phase(t + 1);
       wait_vmem_all();
       wg_barrier();
-      m_phase(t + 1, 1, 0);
+      m_phase(t + 1, 1, 0, n_math);
+      wg_barrier();
+    }
+    for (int u = n_math; u < n_kt; ++u) {
+      if (u + 1 < n_kt) load_k((u + 1) & 1, u + 1);
+      wait_vmem_all();
+      wg_barrier();
       wg_barrier();
     }
   } else {
     wg_barrier();
     for (int t = 0; t < n_kt; t += 2) {
-      m_phase(t - 1, 1, 0);
+      m_phase(t - 1, 1, 0, n_kt);
       wait_vmem_all();
       wg_barrier();
       if (t + 1 < n_kt) load_v(1, t + 1);
       v_phase(t);
       wg_barrier();
       if (t + 1 >= n_kt) break;
-      m_phase(t, 0, 1);
+      m_phase(t, 0, 1, n_kt);
       wait_vmem_all();
       wg_barrier();
       if (t + 2 < n_kt) load_v(0, t + 2);
@@ -659,8 +671,8 @@ __global__ __launch_bounds__(512, 1) void fwd16pp_kernel(FwdArgs a) {
       wg_barrier();
     }
     // P.V of the last tile (its V stage is not the target of the load still in flight).
-    if (n_kt & 1) m_phase(n_kt - 1, 0, 1);
-    else m_phase(n_kt - 1, 1, 0);
+    if (n_kt & 1) m_phase(n_kt - 1, 0, 1, n_kt);
+    else m_phase(n_kt - 1, 1, 0, n_kt);
     wait_vmem_all();
   }
 
